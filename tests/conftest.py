@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long-running CPU oracle work")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The HIP binding, loaded once; fails loudly when the library or GPU is missing."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test selected but torch sees no GPU")
+    import linear_memory_relation_amd as lmr
+    lmr.load()      # raises if the built library is missing
+    return lmr
