@@ -1,0 +1,160 @@
+/*
+ * larard.h -- C ABI of the linear-memory relation-KL library (liblarard.so).
+ *
+ * The operation ("LinearARD: Linear-Memory Attention Distillation for RoPE
+ * Restoration", paper-notes page, section "Key designs", items 1 and 3):
+ * for every head, teacher (t) and student (s) projections X_t, X_s in
+ * R^{n x d} define logits Z_m = scale * X_m X_m^T, a causal mask keeps
+ * j <= i, and R_m = row-softmax(Z_m).  The per-head loss is the row mean of
+ * the forward divergence KL(R_t(i,:) || R_s(i,:)); the student gradient is
+ *     dX_s = scale * (dZ X_s + dZ^T X_s),   dZ = (R_s - R_t) / n,
+ * where both terms land in dX_s because the relation is a self-relation
+ * (X = Y).  Phase 1 stores only the per-row log-sum-exp LSE_m(i); phase 2
+ * recomputes logit tiles on chip and never stores an n x n map, so extra
+ * memory is O(B*H*n).  The teacher is frozen: no teacher gradient exists.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors X_t, X_s are [B, H, n, d] contiguous, row-major (d fastest),
+ *     in bf16 (LARARD_BF16) or fp32 (LARARD_FP32), 16-byte aligned.
+ *     d must be 64 or 128.  B, H >= 1; 0 <= n <= 2^24.
+ *   - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *     library allocates no device memory and keeps no pointer after return.
+ *   - LSE buffers are fp64 [B, H, n] in natural log, 8-byte aligned;
+ *     row_kl is fp32 [B, H, n].  The statistics are fp64 because phase 2
+ *     rebuilds every probability from them: an fp32 LSE near 45 (peaky
+ *     rows) is off by ~4e-6, which shifts a whole probability row by that
+ *     factor and can exceed a nearly vanishing dZ.
+ *   - bf16 inputs run on bf16 MFMA with fp32 accumulation.  fp32 inputs run
+ *     a precision mode that keeps logits, probabilities and statistics in
+ *     fp64 (each dZ row sums to zero, so dZ X_s is a small difference of
+ *     weighted means and fp32 logits alone would cost ~1e-4 of it); it is
+ *     meant for checking and small inputs, not for throughput.
+ *   - dx_s is fp32 [B, H, n, d], 16-byte aligned, and is OVERWRITTEN.
+ *   - scale must be finite and > 0 (the workloads use 1/sqrt(d)).
+ *   - causal != 0 keeps j <= i (diagonal included); causal == 0 keeps all
+ *     n columns (the bidirectional variant).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     stream-ordered and asynchronous; arguments are validated before any
+ *     launch, and on a validation error nothing is launched or written.
+ *     A failing HIP call returns LARARD_E_HIP; its text is available from
+ *     larard_last_error() on the calling thread.
+ *   - The library holds no mutable global state and is thread-safe.
+ */
+#ifndef LARARD_H
+#define LARARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LARARD_OK = 0,
+  LARARD_E_INVALID = 1,     /* null pointer, bad size, bad scale, misalignment */
+  LARARD_E_UNSUPPORTED = 2, /* head dim, dtype or mode not built */
+  LARARD_E_WORKSPACE = 3,   /* workspace too small or misaligned */
+  LARARD_E_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} larard_status;
+
+typedef enum { LARARD_BF16 = 0, LARARD_FP32 = 1 } larard_dtype;
+
+/* How phase 2 produces the column term dZ^T X_s of the gradient.
+ *   SPLIT : a second, column-owned sweep recomputes the logit tiles and adds
+ *           the column term; deterministic, no atomics.
+ *   ATOMIC: the row-owned sweep adds the column term with fp32 atomics;
+ *           one sweep, last-bit run-to-run variation.
+ *   AUTO  : the mode measured fastest for the shape. */
+typedef enum { LARARD_DX_AUTO = 0, LARARD_DX_SPLIT = 1, LARARD_DX_ATOMIC = 2 } larard_dx_mode;
+
+/* Bytes of workspace larard_loss needs: LSE_t and LSE_s (B*H*n fp64 each),
+ * row_kl (B*H*n fp32) and B*H fp64 partial sums, each region 256-byte
+ * aligned: 20*B*H*n + 8*B*H (+ alignment).  O(B*H*n):
+ * the notes page ("Key designs", item 3) stores only per-row statistics.
+ * Returns 0 for invalid sizes. */
+size_t larard_workspace_bytes(larard_dtype dtype, int64_t B, int64_t H, int64_t n);
+
+/* Phase 1 (notes page, "Key designs" item 3; summary page, "Method"):
+ * streams key tiles with an online max/sum and writes
+ *   lse_t[b,h,i] = log sum_{j kept} exp(scale * <x_t,i , x_t,j>)
+ * and likewise lse_s, fp64 [B, H, n].  No other output. */
+larard_status larard_lse_fwd(const void* x_t, const void* x_s, larard_dtype dtype,
+                             int64_t B, int64_t H, int64_t n, int64_t d,
+                             float scale, int causal,
+                             void* lse_t, void* lse_s, void* stream);
+
+/* Phase 2 (notes page, "Key designs" item 3): recomputes the logit tiles,
+ * rebuilds R_t and R_s from lse_t / lse_s (which must come from
+ * larard_lse_fwd with the same inputs and arguments), and writes
+ *   row_kl[b,h,i] = KL(R_t(i,:) || R_s(i,:))          (fp32, not scaled)
+ *   dx_s[b,h,i,:] = loss_scale * scale * (dZ X_s + dZ^T X_s)[i,:]
+ * with dZ = (R_s - R_t)/n.  loss_scale = 1 is the pages' convention (heads
+ * summed); 1/(B*H) gives a head mean.  dx_s == NULL computes row_kl only.
+ * dx_mode is a larard_dx_mode. */
+larard_status larard_kl_bwd(const void* x_t, const void* x_s, larard_dtype dtype,
+                            int64_t B, int64_t H, int64_t n, int64_t d,
+                            float scale, int causal,
+                            const void* lse_t, const void* lse_s,
+                            float loss_scale, float* row_kl, float* dx_s,
+                            int dx_mode, void* stream);
+
+/* The two halves of larard_kl_bwd in split mode, for callers that schedule
+ * them separately (e.g. to overlap maps on several streams).
+ * larard_kl_bwd_rows: row-owned sweep; writes row_kl and STORES the row term
+ *   loss_scale * scale * (dZ X_s)[i,:] into dx_s (dx_s == NULL: row_kl only).
+ * larard_kl_bwd_cols: column-owned sweep; ADDS the column term
+ *   loss_scale * scale * (dZ^T X_s)[j,:] into dx_s, which must already hold
+ *   the row term of the same call sequence.  Running rows then cols on one
+ *   stream equals larard_kl_bwd with LARARD_DX_SPLIT, bit for bit. */
+larard_status larard_kl_bwd_rows(const void* x_t, const void* x_s, larard_dtype dtype,
+                                 int64_t B, int64_t H, int64_t n, int64_t d,
+                                 float scale, int causal,
+                                 const void* lse_t, const void* lse_s,
+                                 float loss_scale, float* row_kl, float* dx_s, void* stream);
+larard_status larard_kl_bwd_cols(const void* x_t, const void* x_s, larard_dtype dtype,
+                                 int64_t B, int64_t H, int64_t n, int64_t d,
+                                 float scale, int causal,
+                                 const void* lse_t, const void* lse_s,
+                                 float loss_scale, float* dx_s, void* stream);
+
+/* Loss reduction (notes page, "Key designs" item 1: row mean, summed over
+ * heads): *loss = loss_scale * sum_{b,h} (1/n) sum_i row_kl[b,h,i], summed in
+ * fp64 in a fixed order (bitwise reproducible).  partials: device scratch of
+ * B*H doubles, 8-byte aligned.  n == 0 writes *loss = 0. */
+larard_status larard_reduce_loss(const float* row_kl, int64_t B, int64_t H, int64_t n,
+                                 float loss_scale, double* partials, float* loss, void* stream);
+
+/* Whole path for one relation map: phase 1, phase 2 and a deterministic
+ * fp64 reduction.  Writes
+ *   *loss = loss_scale * sum_{b,h} (1/n) sum_i KL_i        (device fp32 scalar)
+ * and dx_s as in larard_kl_bwd (NULL = loss only).  The workspace (device,
+ * 256-byte aligned, >= larard_workspace_bytes(dtype,B,H,n)) holds LSE_t, LSE_s,
+ * row_kl and partial sums; after return-and-sync it contains them in that
+ * order (see larard_workspace_layout).  n == 0 writes *loss = 0. */
+larard_status larard_loss(const void* x_t, const void* x_s, larard_dtype dtype,
+                          int64_t B, int64_t H, int64_t n, int64_t d,
+                          float scale, int causal, float loss_scale,
+                          void* workspace, size_t workspace_bytes,
+                          float* loss, float* dx_s, int dx_mode, void* stream);
+
+/* Byte offsets of the regions larard_loss carves from its workspace:
+ * off[0] = lse_t, off[1] = lse_s, off[2] = row_kl, off[3] = fp64 partials.
+ * Returns LARARD_E_INVALID for invalid sizes. */
+larard_status larard_workspace_layout(larard_dtype dtype, int64_t B, int64_t H, int64_t n,
+                                      size_t off[4]);
+
+/* Static description of a status code. */
+const char* larard_status_str(larard_status status);
+
+/* Text of the last LARARD_E_HIP / validation failure on this thread ("" if none). */
+const char* larard_last_error(void);
+
+/* Library version string, e.g. "larard 0.1.0 gfx950". */
+const char* larard_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LARARD_H */

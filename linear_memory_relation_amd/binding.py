@@ -1,0 +1,207 @@
+"""ctypes binding of liblarard.so: argument marshalling only.
+
+Every step of the relation-KL path runs in the HIP kernels behind the C ABI
+(include/larard.h).  PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblarard.so")
+
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, 1, 2, 3, 4
+BF16, FP32 = 0, 1
+DX_AUTO, DX_SPLIT, DX_ATOMIC = 0, 1, 2
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class LarardError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {detail}")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblarard.so (built by linear_memory_relation_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"liblarard.so not found at {path}; build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    lib.larard_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    lib.larard_workspace_bytes.restype = ctypes.c_size_t
+    lib.larard_workspace_layout.argtypes = [i32, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.larard_workspace_layout.restype = i32
+    lib.larard_lse_fwd.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, vp]
+    lib.larard_lse_fwd.restype = i32
+    lib.larard_kl_bwd.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, f32, vp, vp, i32, vp]
+    lib.larard_kl_bwd.restype = i32
+    lib.larard_kl_bwd_rows.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, f32, vp, vp, vp]
+    lib.larard_kl_bwd_rows.restype = i32
+    lib.larard_kl_bwd_cols.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, f32, vp, vp]
+    lib.larard_kl_bwd_cols.restype = i32
+    lib.larard_reduce_loss.argtypes = [vp, i64, i64, i64, f32, vp, vp, vp]
+    lib.larard_reduce_loss.restype = i32
+    lib.larard_loss.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, f32, vp, ctypes.c_size_t,
+                                vp, vp, i32, vp]
+    lib.larard_loss.restype = i32
+    lib.larard_status_str.argtypes = [i32]
+    lib.larard_status_str.restype = ctypes.c_char_p
+    lib.larard_last_error.argtypes = []
+    lib.larard_last_error.restype = ctypes.c_char_p
+    lib.larard_version.argtypes = []
+    lib.larard_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        lib = load()
+        raise LarardError(status, where, f"{lib.larard_status_str(status).decode()} -- "
+                                         f"{lib.larard_last_error().decode()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _shape(xt: torch.Tensor, xs: torch.Tensor):
+    if xt.dim() != 4 or xt.shape != xs.shape or xt.dtype != xs.dtype:
+        raise ValueError("x_t and x_s must both be [B, H, n, d] with the same dtype")
+    if not (xt.is_cuda and xs.is_cuda and xt.is_contiguous() and xs.is_contiguous()):
+        raise ValueError("x_t and x_s must be contiguous GPU tensors")
+    return tuple(int(v) for v in xt.shape)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def workspace_bytes(B: int, H: int, n: int, dtype: int = BF16) -> int:
+    return int(load().larard_workspace_bytes(dtype, B, H, n))
+
+
+def workspace_layout(B: int, H: int, n: int, dtype: int = BF16):
+    off = (ctypes.c_size_t * 4)()
+    _check(load().larard_workspace_layout(dtype, B, H, n, off), "larard_workspace_layout")
+    return [int(v) for v in off]
+
+
+def stat_dtype(x: torch.Tensor) -> torch.dtype:
+    """Element type of the LSE statistics (fp64 for every input type)."""
+    return torch.float64
+
+
+def lse_fwd(xt: torch.Tensor, xs: torch.Tensor, scale: Optional[float] = None, causal: bool = True,
+            lse_t: Optional[torch.Tensor] = None, lse_s: Optional[torch.Tensor] = None
+            ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Phase 1: per-row log-sum-exp of teacher and student logits, fp64 [B, H, n]."""
+    B, H, n, d = _shape(xt, xs)
+    scale = default_scale(d) if scale is None else float(scale)
+    if lse_t is None:
+        lse_t = torch.empty((B, H, n), dtype=stat_dtype(xt), device=xt.device)
+    if lse_s is None:
+        lse_s = torch.empty((B, H, n), dtype=stat_dtype(xt), device=xt.device)
+    st = load().larard_lse_fwd(_ptr(xt), _ptr(xs), _dtype_code(xt), B, H, n, d, scale, int(causal),
+                               _ptr(lse_t), _ptr(lse_s), _stream())
+    _check(st, "larard_lse_fwd")
+    return lse_t, lse_s
+
+
+def kl_bwd(xt: torch.Tensor, xs: torch.Tensor, lse_t: torch.Tensor, lse_s: torch.Tensor,
+           scale: Optional[float] = None, causal: bool = True, loss_scale: float = 1.0,
+           need_dx: bool = True, dx_mode: int = DX_AUTO, row_kl: Optional[torch.Tensor] = None,
+           dx: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Phase 2: per-row KL(R_t || R_s) (fp32 [B,H,n]) and dX_s (fp32 [B,H,n,d] or None)."""
+    B, H, n, d = _shape(xt, xs)
+    scale = default_scale(d) if scale is None else float(scale)
+    if row_kl is None:
+        row_kl = torch.empty((B, H, n), dtype=torch.float32, device=xt.device)
+    if need_dx and dx is None:
+        dx = torch.empty((B, H, n, d), dtype=torch.float32, device=xt.device)
+    if not need_dx:
+        dx = None
+    st = load().larard_kl_bwd(_ptr(xt), _ptr(xs), _dtype_code(xt), B, H, n, d, scale, int(causal),
+                              _ptr(lse_t), _ptr(lse_s), float(loss_scale), _ptr(row_kl), _ptr(dx),
+                              int(dx_mode), _stream())
+    _check(st, "larard_kl_bwd")
+    return row_kl, dx
+
+
+def kl_bwd_rows(xt, xs, lse_t, lse_s, row_kl, dx=None, scale=None, causal=True, loss_scale=1.0):
+    """Row-owned half of phase 2: writes row_kl, stores the row term into dx (if given)."""
+    B, H, n, d = _shape(xt, xs)
+    scale = default_scale(d) if scale is None else float(scale)
+    st = load().larard_kl_bwd_rows(_ptr(xt), _ptr(xs), _dtype_code(xt), B, H, n, d, scale, int(causal),
+                                   _ptr(lse_t), _ptr(lse_s), float(loss_scale), _ptr(row_kl), _ptr(dx),
+                                   _stream())
+    _check(st, "larard_kl_bwd_rows")
+
+
+def kl_bwd_cols(xt, xs, lse_t, lse_s, dx, scale=None, causal=True, loss_scale=1.0):
+    """Column-owned half of phase 2: adds the column term into dx."""
+    B, H, n, d = _shape(xt, xs)
+    scale = default_scale(d) if scale is None else float(scale)
+    st = load().larard_kl_bwd_cols(_ptr(xt), _ptr(xs), _dtype_code(xt), B, H, n, d, scale, int(causal),
+                                   _ptr(lse_t), _ptr(lse_s), float(loss_scale), _ptr(dx), _stream())
+    _check(st, "larard_kl_bwd_cols")
+
+
+def reduce_loss(row_kl: torch.Tensor, partials: torch.Tensor, out: torch.Tensor, loss_scale: float = 1.0):
+    """loss = loss_scale * sum over heads of the row mean of row_kl ([B, H, n] fp32)."""
+    B, H, n = (int(v) for v in row_kl.shape)
+    st = load().larard_reduce_loss(_ptr(row_kl), B, H, n, float(loss_scale), _ptr(partials), _ptr(out),
+                                   _stream())
+    _check(st, "larard_reduce_loss")
+
+
+def loss(xt: torch.Tensor, xs: torch.Tensor, scale: Optional[float] = None, causal: bool = True,
+         loss_scale: float = 1.0, need_dx: bool = True, dx_mode: int = DX_AUTO,
+         workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+         dx: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Whole path for one relation map: returns (loss as a 0-d fp32 device tensor, dX_s or None)."""
+    B, H, n, d = _shape(xt, xs)
+    scale = default_scale(d) if scale is None else float(scale)
+    nbytes = workspace_bytes(B, H, n, _dtype_code(xt))
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=xt.device)
+    if out is None:
+        out = torch.empty((), dtype=torch.float32, device=xt.device)
+    if need_dx and dx is None:
+        dx = torch.empty((B, H, n, d), dtype=torch.float32, device=xt.device)
+    if not need_dx:
+        dx = None
+    st = load().larard_loss(_ptr(xt), _ptr(xs), _dtype_code(xt), B, H, n, d, scale, int(causal),
+                            float(loss_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _ptr(out), _ptr(dx), int(dx_mode), _stream())
+    _check(st, "larard_loss")
+    return out, dx
+
+
+def version() -> str:
+    return load().larard_version().decode()

@@ -1,0 +1,268 @@
+// C ABI of liblarard.so (declared in include/larard.h): argument validation,
+// workspace carving and kernel dispatch.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "larard.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+constexpr int kOwnRows = 128;   // rows owned by one workgroup (see kernels.hip)
+
+larard_status fail(larard_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+larard_status fail(larard_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+larard_status hip_fail(hipError_t e, const char* what) {
+  return fail(LARARD_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// LSE statistics are fp64 for every input type.
+size_t stat_bytes(larard_dtype) { return sizeof(double); }
+
+// Validation shared by every entry point; touches no HIP state.
+larard_status check_common(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
+                           int64_t n, int64_t d, float scale) {
+  if (B < 1 || H < 1) return fail(LARARD_E_INVALID, "B and H must be >= 1 (got B=%lld H=%lld)", (long long)B, (long long)H);
+  if (n < 0 || n > kMaxN) return fail(LARARD_E_INVALID, "n must be in [0, 2^24] (got %lld)", (long long)n);
+  if (B > kMaxGrid / H) return fail(LARARD_E_INVALID, "B*H too large");
+  const int64_t bh = B * H;
+  const int64_t nblk = (n + kOwnRows - 1) / kOwnRows;
+  if (nblk > 0 && bh > kMaxGrid / nblk) return fail(LARARD_E_INVALID, "B*H*ceil(n/128) exceeds the launch grid");
+  if (dtype != LARARD_BF16 && dtype != LARARD_FP32) return fail(LARARD_E_UNSUPPORTED, "dtype %d not supported", (int)dtype);
+  if (d != 64 && d != 128) return fail(LARARD_E_UNSUPPORTED, "head dim d=%lld not supported (64 or 128)", (long long)d);
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(LARARD_E_INVALID, "scale must be finite and > 0");
+  if (n > 0) {
+    if (x_t == nullptr || x_s == nullptr) return fail(LARARD_E_INVALID, "x_t / x_s must not be NULL");
+    if (!aligned(x_t, 16) || !aligned(x_s, 16)) return fail(LARARD_E_INVALID, "x_t / x_s must be 16-byte aligned");
+  }
+  return LARARD_OK;
+}
+
+lmr::SweepArgs make_args(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H, int64_t n,
+                         int64_t d, float scale, int causal) {
+  lmr::SweepArgs a{};
+  a.xt = x_t;
+  a.xs = x_s;
+  a.bh = B * H;
+  a.n = (int)n;
+  a.d = (int)d;
+  a.fp32 = dtype == LARARD_FP32 ? 1 : 0;
+  a.causal = causal ? 1 : 0;
+  a.scale = scale;
+  return a;
+}
+
+larard_status check_dx_mode(int dx_mode) {
+  if (dx_mode == LARARD_DX_AUTO || dx_mode == LARARD_DX_SPLIT) return LARARD_OK;
+  if (dx_mode == LARARD_DX_ATOMIC) return fail(LARARD_E_UNSUPPORTED, "dx_mode ATOMIC is not built");
+  return fail(LARARD_E_INVALID, "unknown dx_mode %d", dx_mode);
+}
+
+// Phase-2 launches (inputs already validated).
+larard_status run_kl_bwd(lmr::SweepArgs a, float loss_scale, hipStream_t st) {
+  a.grad_scale = loss_scale * a.scale / (float)a.n;
+  a.grad_scale_d = (double)loss_scale * (double)a.scale / (double)a.n;
+  hipError_t e = lmr::launch_kl_row(a, st);
+  if (e != hipSuccess) return hip_fail(e, "kl_bwd row sweep launch");
+  if (a.dx != nullptr) {
+    e = lmr::launch_kl_col(a, st);
+    if (e != hipSuccess) return hip_fail(e, "kl_bwd column sweep launch");
+  }
+  return LARARD_OK;
+}
+
+// Validation shared by the phase-2 entry points; fills *out on success.
+larard_status check_phase2(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H, int64_t n,
+                           int64_t d, float scale, int causal, const void* lse_t, const void* lse_s,
+                           float loss_scale, lmr::SweepArgs* out) {
+  larard_status s = check_common(x_t, x_s, dtype, B, H, n, d, scale);
+  if (s != LARARD_OK) return s;
+  if (!std::isfinite(loss_scale)) return fail(LARARD_E_INVALID, "loss_scale must be finite");
+  if (n == 0) return LARARD_OK;
+  if (lse_t == nullptr || lse_s == nullptr) return fail(LARARD_E_INVALID, "lse_t / lse_s must not be NULL");
+  if (!aligned(lse_t, stat_bytes(dtype)) || !aligned(lse_s, stat_bytes(dtype)))
+    return fail(LARARD_E_INVALID, "lse buffers must be aligned to their element size");
+  *out = make_args(x_t, x_s, dtype, B, H, n, d, scale, causal);
+  out->lse_t = const_cast<void*>(lse_t);
+  out->lse_s = const_cast<void*>(lse_s);
+  out->grad_scale = loss_scale * scale / (float)n;
+  out->grad_scale_d = (double)loss_scale * (double)scale / (double)n;
+  return LARARD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t larard_workspace_bytes(larard_dtype dtype, int64_t B, int64_t H, int64_t n) {
+  size_t off[4];
+  if (larard_workspace_layout(dtype, B, H, n, off) != LARARD_OK) return 0;
+  return off[3] + align256((size_t)(B * H) * sizeof(double));
+}
+
+larard_status larard_workspace_layout(larard_dtype dtype, int64_t B, int64_t H, int64_t n, size_t off[4]) {
+  if (off == nullptr || B < 1 || H < 1 || n < 0 || n > kMaxN || B > kMaxGrid / H)
+    return fail(LARARD_E_INVALID, "invalid sizes for workspace layout");
+  if (dtype != LARARD_BF16 && dtype != LARARD_FP32) return fail(LARARD_E_UNSUPPORTED, "dtype %d not supported", (int)dtype);
+  const size_t rows = (size_t)(B * H) * (size_t)n;
+  const size_t stat = align256(rows * stat_bytes(dtype));
+  off[0] = 0;
+  off[1] = stat;
+  off[2] = 2 * stat;
+  off[3] = 2 * stat + align256(rows * sizeof(float));
+  return LARARD_OK;
+}
+
+larard_status larard_lse_fwd(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
+                             int64_t n, int64_t d, float scale, int causal, void* lse_t, void* lse_s,
+                             void* stream) {
+  larard_status s = check_common(x_t, x_s, dtype, B, H, n, d, scale);
+  if (s != LARARD_OK) return s;
+  if (n == 0) return LARARD_OK;
+  if (lse_t == nullptr || lse_s == nullptr) return fail(LARARD_E_INVALID, "lse_t / lse_s must not be NULL");
+  if (!aligned(lse_t, stat_bytes(dtype)) || !aligned(lse_s, stat_bytes(dtype)))
+    return fail(LARARD_E_INVALID, "lse buffers must be aligned to their element size");
+  lmr::SweepArgs a = make_args(x_t, x_s, dtype, B, H, n, d, scale, causal);
+  a.lse_t = lse_t;
+  a.lse_s = lse_s;
+  const hipError_t e = lmr::launch_lse_fwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "lse_fwd launch");
+  return LARARD_OK;
+}
+
+larard_status larard_kl_bwd(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
+                            int64_t n, int64_t d, float scale, int causal, const void* lse_t,
+                            const void* lse_s, float loss_scale, float* row_kl, float* dx_s, int dx_mode,
+                            void* stream) {
+  lmr::SweepArgs a;
+  larard_status s = check_phase2(x_t, x_s, dtype, B, H, n, d, scale, causal, lse_t, lse_s, loss_scale, &a);
+  if (s != LARARD_OK) return s;
+  if ((s = check_dx_mode(dx_mode)) != LARARD_OK) return s;
+  if (n == 0) return LARARD_OK;
+  if (row_kl == nullptr || !aligned(row_kl, 4)) return fail(LARARD_E_INVALID, "row_kl must be a 4-byte aligned pointer");
+  if (dx_s != nullptr && !aligned(dx_s, 16)) return fail(LARARD_E_INVALID, "dx_s must be 16-byte aligned");
+  a.row_kl = row_kl;
+  a.dx = dx_s;
+  return run_kl_bwd(a, loss_scale, static_cast<hipStream_t>(stream));
+}
+
+larard_status larard_loss(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
+                          int64_t n, int64_t d, float scale, int causal, float loss_scale, void* workspace,
+                          size_t workspace_bytes, float* loss, float* dx_s, int dx_mode, void* stream) {
+  larard_status s = check_common(x_t, x_s, dtype, B, H, n, d, scale);
+  if (s != LARARD_OK) return s;
+  if ((s = check_dx_mode(dx_mode)) != LARARD_OK) return s;
+  if (!std::isfinite(loss_scale)) return fail(LARARD_E_INVALID, "loss_scale must be finite");
+  if (loss == nullptr || !aligned(loss, 4)) return fail(LARARD_E_INVALID, "loss must be a 4-byte aligned device pointer");
+  if (dx_s != nullptr && !aligned(dx_s, 16)) return fail(LARARD_E_INVALID, "dx_s must be 16-byte aligned");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n == 0) {
+    const hipError_t e = lmr::launch_zero_scalar(loss, st);
+    return e == hipSuccess ? LARARD_OK : hip_fail(e, "zero loss launch");
+  }
+  size_t off[4];
+  if ((s = larard_workspace_layout(dtype, B, H, n, off)) != LARARD_OK) return s;
+  const size_t need = larard_workspace_bytes(dtype, B, H, n);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(LARARD_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(LARARD_E_WORKSPACE, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  void* lse_t = ws + off[0];
+  void* lse_s = ws + off[1];
+  float* row_kl = reinterpret_cast<float*>(ws + off[2]);
+  double* partials = reinterpret_cast<double*>(ws + off[3]);
+
+  lmr::SweepArgs a = make_args(x_t, x_s, dtype, B, H, n, d, scale, causal);
+  a.lse_t = lse_t;
+  a.lse_s = lse_s;
+  hipError_t e = lmr::launch_lse_fwd(a, st);
+  if (e != hipSuccess) return hip_fail(e, "lse_fwd launch");
+  a.row_kl = row_kl;
+  a.dx = dx_s;
+  if ((s = run_kl_bwd(a, loss_scale, st)) != LARARD_OK) return s;
+  e = lmr::launch_reduce(row_kl, a.bh, a.n, loss_scale, partials, loss, st);
+  if (e != hipSuccess) return hip_fail(e, "loss reduction launch");
+  return LARARD_OK;
+}
+
+larard_status larard_kl_bwd_rows(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
+                                 int64_t n, int64_t d, float scale, int causal, const void* lse_t,
+                                 const void* lse_s, float loss_scale, float* row_kl, float* dx_s, void* stream) {
+  lmr::SweepArgs a;
+  larard_status s = check_phase2(x_t, x_s, dtype, B, H, n, d, scale, causal, lse_t, lse_s, loss_scale, &a);
+  if (s != LARARD_OK || n == 0) return s;
+  if (row_kl == nullptr || !aligned(row_kl, 4)) return fail(LARARD_E_INVALID, "row_kl must be a 4-byte aligned pointer");
+  if (dx_s != nullptr && !aligned(dx_s, 16)) return fail(LARARD_E_INVALID, "dx_s must be 16-byte aligned");
+  a.row_kl = row_kl;
+  a.dx = dx_s;
+  const hipError_t e = lmr::launch_kl_row(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LARARD_OK : hip_fail(e, "kl_bwd row sweep launch");
+}
+
+larard_status larard_kl_bwd_cols(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
+                                 int64_t n, int64_t d, float scale, int causal, const void* lse_t,
+                                 const void* lse_s, float loss_scale, float* dx_s, void* stream) {
+  lmr::SweepArgs a;
+  larard_status s = check_phase2(x_t, x_s, dtype, B, H, n, d, scale, causal, lse_t, lse_s, loss_scale, &a);
+  if (s != LARARD_OK || n == 0) return s;
+  if (dx_s == nullptr || !aligned(dx_s, 16)) return fail(LARARD_E_INVALID, "dx_s must be a 16-byte aligned pointer");
+  a.dx = dx_s;
+  const hipError_t e = lmr::launch_kl_col(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LARARD_OK : hip_fail(e, "kl_bwd column sweep launch");
+}
+
+larard_status larard_reduce_loss(const float* row_kl, int64_t B, int64_t H, int64_t n, float loss_scale,
+                                 double* partials, float* loss, void* stream) {
+  if (B < 1 || H < 1 || n < 0 || n > kMaxN || B > kMaxGrid / H) return fail(LARARD_E_INVALID, "invalid sizes");
+  if (!std::isfinite(loss_scale)) return fail(LARARD_E_INVALID, "loss_scale must be finite");
+  if (loss == nullptr || !aligned(loss, 4)) return fail(LARARD_E_INVALID, "loss must be a 4-byte aligned pointer");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n == 0) {
+    const hipError_t e = lmr::launch_zero_scalar(loss, st);
+    return e == hipSuccess ? LARARD_OK : hip_fail(e, "zero loss launch");
+  }
+  if (row_kl == nullptr || !aligned(row_kl, 4)) return fail(LARARD_E_INVALID, "row_kl must be a 4-byte aligned pointer");
+  if (partials == nullptr || !aligned(partials, 8)) return fail(LARARD_E_INVALID, "partials must be an 8-byte aligned pointer");
+  const hipError_t e = lmr::launch_reduce(row_kl, B * H, (int)n, loss_scale, partials, loss, st);
+  return e == hipSuccess ? LARARD_OK : hip_fail(e, "loss reduction launch");
+}
+
+const char* larard_status_str(larard_status status) {
+  switch (status) {
+    case LARARD_OK: return "LARARD_OK";
+    case LARARD_E_INVALID: return "LARARD_E_INVALID: invalid argument";
+    case LARARD_E_UNSUPPORTED: return "LARARD_E_UNSUPPORTED: unsupported head dim, dtype or mode";
+    case LARARD_E_WORKSPACE: return "LARARD_E_WORKSPACE: workspace too small or misaligned";
+    case LARARD_E_HIP: return "LARARD_E_HIP: HIP runtime error";
+  }
+  return "unknown larard_status";
+}
+
+const char* larard_last_error(void) { return g_last_error.c_str(); }
+
+const char* larard_version(void) { return "larard 0.1.0 gfx950"; }
+
+}  // extern "C"

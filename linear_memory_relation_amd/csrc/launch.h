@@ -1,0 +1,44 @@
+// Internal launcher interface between the C ABI (api.cpp) and the gfx950
+// kernels (kernels.hip).  Not installed; the public interface is larard.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmr {
+
+// Geometry and arguments of one launch over B*H heads of one relation map.
+struct SweepArgs {
+  const void* xt;        // [BH, n, d] teacher, bf16 bits or fp32
+  const void* xs;        // [BH, n, d] student
+  void* lse_t;           // [BH, n] fp32 (bf16 inputs) or fp64 (fp32 inputs)
+  void* lse_s;           // [BH, n]
+  float* row_kl;         // [BH, n]  phase-2 output (may be null for COL sweeps)
+  float* dx;             // [BH, n, d] fp32 gradient (null = no gradient)
+  int64_t bh;            // number of heads B*H
+  int n;                 // sequence length
+  int d;                 // head dim (64 or 128)
+  int fp32;              // 1: fp32 inputs, 0: bf16
+  int causal;            // 1: keep j <= i
+  float scale;           // logit scale s
+  float grad_scale;      // loss_scale * s / n, applied to the dZ contractions
+  double grad_scale_d;   // the same factor in fp64 (fp32-input path)
+};
+
+hipError_t launch_lse_fwd(const SweepArgs& a, hipStream_t st);
+// Row-owned phase-2 sweep: row KL and the row term dZ X_s (stored, not added).
+hipError_t launch_kl_row(const SweepArgs& a, hipStream_t st);
+// Column-owned phase-2 sweep: adds the column term dZ^T X_s into dx.
+hipError_t launch_kl_col(const SweepArgs& a, hipStream_t st);
+// fp32-input path (fp64 arithmetic on the vector ALUs), in wide.hip.
+hipError_t launch_wide_lse_fwd(const SweepArgs& a, hipStream_t st);
+hipError_t launch_wide_kl_row(const SweepArgs& a, hipStream_t st);
+hipError_t launch_wide_kl_col(const SweepArgs& a, hipStream_t st);
+// loss = loss_scale/n * sum over heads and rows of row_kl, reduced in fp64
+// in a fixed order (deterministic).  partials: [bh] fp64 scratch.
+hipError_t launch_reduce(const float* row_kl, int64_t bh, int n, float loss_scale,
+                         double* partials, float* loss, hipStream_t st);
+// *loss = 0 (used when n == 0).
+hipError_t launch_zero_scalar(float* loss, hipStream_t st);
+
+}  // namespace lmr

@@ -24,8 +24,10 @@ Readings (the pages print no RoPE formula):
 """
 from __future__ import annotations
 
+import concurrent.futures as _cf
 import dataclasses
 import math
+import os
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -186,16 +188,30 @@ def _student_tables(w: Workload, n: int):
     return rope_tables(n, w.d, base_s, pos_scale=1.0)
 
 
+def _per_head(fn, B: int, H: int) -> None:
+    """Run fn(b, h) for every head on a small thread pool (numpy releases the GIL)."""
+    jobs = [(b, h) for b in range(B) for h in range(H)]
+    workers = max(1, min(8, os.cpu_count() or 1, len(jobs)))
+    if workers == 1:
+        for bh in jobs:
+            fn(*bh)
+        return
+    with _cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda bh: fn(*bh), jobs))
+
+
 def _rope_pair(p32: np.ndarray, w: Workload, tabs, dtype: str):
     """Teacher and student storage arrays for projections p32 [B, H, n, d]."""
     (ct, st), (cs, ss) = tabs
     xt = np.empty(p32.shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
     xs = np.empty_like(xt)
-    for b in range(p32.shape[0]):          # per head keeps float64 temporaries small
-        for h in range(p32.shape[1]):
-            p = p32[b, h].astype(np.float64)
-            xt[b, h] = _store(apply_rope(p, ct, st), dtype)
-            xs[b, h] = _store(apply_rope(p, cs, ss), dtype)
+
+    def one(b, h):                          # per head keeps float64 temporaries small
+        p = p32[b, h].astype(np.float64)
+        xt[b, h] = _store(apply_rope(p, ct, st), dtype)
+        xs[b, h] = _store(apply_rope(p, cs, ss), dtype)
+
+    _per_head(one, p32.shape[0], p32.shape[1])
     return xt, xs
 
 
@@ -240,10 +256,12 @@ def make_inputs(w: Workload, maps: Optional[List[str]] = None) -> Dict[str, MapI
     if "V" in maps:
         xt = np.empty(v_t.shape, dtype=np.uint16 if w.dtype == "bf16" else np.float32)
         xs = np.empty_like(xt)
-        for b in range(B):
-            for h in range(hv):
-                vt = v_t[b, h].astype(np.float64)
-                xt[b, h] = _store(vt, w.dtype)
-                xs[b, h] = _store(vt + w.v_noise * eps[b, h].astype(np.float64), w.dtype)
+
+        def one(b, h):
+            vt = v_t[b, h].astype(np.float64)
+            xt[b, h] = _store(vt, w.dtype)
+            xs[b, h] = _store(vt + w.v_noise * eps[b, h].astype(np.float64), w.dtype)
+
+        _per_head(one, B, hv)
         out["V"] = MapInputs("V", xt, xs, w.dtype)
     return out

@@ -1,0 +1,118 @@
+"""C-ABI contract tests that need no GPU: exports, workspace sizing, validation.
+
+Validation runs before any HIP call, so invalid arguments are rejected here
+without a device.  No call in this file reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "larard.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import linear_memory_relation_amd as lmr
+    return lmr.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(larard_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"larard_lse_fwd", "larard_kl_bwd", "larard_loss", "larard_workspace_bytes"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    import linear_memory_relation_amd as lmr
+    assert "gfx950" in lmr.version()
+    for code in range(5):
+        assert lib.larard_status_str(code).decode().startswith("LARARD_")
+
+
+def test_workspace_is_linear_in_bhn(lib):
+    import linear_memory_relation_amd as lmr
+    up = lambda v: -(-v // 256) * 256
+    for B, H, n in [(1, 32, 16384), (2, 8, 8192), (1, 1, 1), (3, 5, 129)]:
+        rows = B * H * n
+        for dt in (lmr.BF16, lmr.FP32):      # fp64 statistics for every input type
+            nb = lmr.workspace_bytes(B, H, n, dt)
+            off = lmr.workspace_layout(B, H, n, dt)
+            assert off == [0, up(8 * rows), 2 * up(8 * rows), 2 * up(8 * rows) + up(4 * rows)]
+            assert nb == off[3] + up(8 * B * H)
+            assert nb <= 20 * rows + 8 * B * H + 4 * 256      # O(BHn) bound
+    assert lmr.workspace_bytes(0, 1, 4) == 0
+    assert lmr.workspace_bytes(1, 1, -1) == 0
+    assert lmr.workspace_bytes(1, 1, 4, 5) == 0
+
+
+FAKE = 1 << 20          # 16-byte aligned non-null address; never dereferenced
+
+
+def _lse(lib, **kw):
+    a = dict(xt=FAKE, xs=FAKE, dt=0, B=1, H=1, n=64, d=128, scale=0.1, causal=1, lt=FAKE, ls=FAKE)
+    a.update(kw)
+    return lib.larard_lse_fwd(a["xt"], a["xs"], a["dt"], a["B"], a["H"], a["n"], a["d"], a["scale"],
+                              a["causal"], a["lt"], a["ls"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(xt=None), 1), (dict(xs=None), 1), (dict(xt=FAKE + 8), 1), (dict(B=0), 1), (dict(H=-1), 1),
+    (dict(n=-1), 1), (dict(n=(1 << 24) + 1), 1), (dict(d=96), 2), (dict(d=256), 2), (dict(dt=7), 2),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=0.0), 1),
+    (dict(scale=-0.5), 1), (dict(lt=None), 1), (dict(ls=FAKE + 2), 1),
+    (dict(dt=1, lt=FAKE + 4), 1), (dict(lt=FAKE + 4), 1),   # fp64 statistics: 8-byte alignment
+])
+def test_lse_fwd_validation(lib, kw, code):
+    assert _lse(lib, **kw) == code
+    assert lib.larard_last_error().decode() != ""
+
+
+def test_empty_sequence_is_a_noop(lib):
+    # n == 0 launches nothing and touches no pointer.
+    assert _lse(lib, n=0, xt=None, xs=None, lt=None, ls=None) == 0
+    st = lib.larard_kl_bwd(None, None, 0, 1, 1, 0, 64, 0.1, 1, None, None, 1.0, None, None, 0, None)
+    assert st == 0
+
+
+def _bwd(lib, **kw):
+    a = dict(xt=FAKE, xs=FAKE, dt=0, B=1, H=2, n=64, d=64, scale=0.1, causal=1, lt=FAKE, ls=FAKE,
+             lscale=1.0, rk=FAKE, dx=FAKE, mode=0)
+    a.update(kw)
+    return lib.larard_kl_bwd(a["xt"], a["xs"], a["dt"], a["B"], a["H"], a["n"], a["d"], a["scale"],
+                             a["causal"], a["lt"], a["ls"], a["lscale"], a["rk"], a["dx"], a["mode"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rk=None), 1), (dict(lt=None), 1), (dict(dx=FAKE + 4), 1), (dict(mode=9), 1),
+    (dict(lscale=float("nan")), 1), (dict(d=32), 2),
+])
+def test_kl_bwd_validation(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+
+
+def _loss(lib, ws=FAKE, wsb=1 << 30, **kw):
+    a = dict(xt=FAKE, xs=FAKE, dt=0, B=1, H=2, n=64, d=128, scale=0.1, causal=1, lscale=1.0,
+             loss=FAKE, dx=FAKE, mode=0)
+    a.update(kw)
+    return lib.larard_loss(a["xt"], a["xs"], a["dt"], a["B"], a["H"], a["n"], a["d"], a["scale"],
+                           a["causal"], a["lscale"], ws, wsb, a["loss"], a["dx"], a["mode"], None)
+
+
+def test_loss_workspace_checks(lib):
+    import linear_memory_relation_amd as lmr
+    need = lmr.workspace_bytes(1, 2, 64)
+    assert _loss(lib, wsb=lmr.workspace_bytes(1, 2, 64, lmr.FP32) - 1, dt=1) == 3
+    assert _loss(lib, wsb=need - 1) == 3
+    assert _loss(lib, ws=None) == 3
+    assert _loss(lib, ws=FAKE + 16) == 3          # not 256-byte aligned
+    assert _loss(lib, loss=None) == 1
+    assert _loss(lib, xt=None) == 1

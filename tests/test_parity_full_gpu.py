@@ -1,0 +1,87 @@
+"""Full-size parity in the benchmark's launch configuration, on sampled outputs.
+
+Each workload is run exactly as bench.py runs it (one `loss` call per relation
+map over all heads).  The fp64 oracle cannot hold the dense n x n maps at
+these sizes, so it computes sampled outputs one by one from their
+definitions: every row's LSE of a sampled head, the KL of sampled rows and
+the gradient of sampled rows (which needs the oracle's own LSE of all rows).
+Properties that hold at any size are checked on the whole output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as si
+from helpers import to_device
+
+pytestmark = pytest.mark.gpu
+
+EPS32 = 2.0 ** -24
+WORKLOADS = ["llama2_4k", "llama3_gqa_8k", "llama2_16k", "llama2_32k"]
+
+
+def _rows(n, rng):
+    fixed = [0, 1, 2, 63, 64, 127, 128, 129, n // 2, n - 65, n - 64, n - 2, n - 1]
+    return sorted(set([r for r in fixed if 0 <= r < n] + list(rng.choice(n, 12, replace=False))))
+
+
+def _head_oracle(xt, xs, s, rows):
+    n = xt.shape[0]
+    lt = np.concatenate([oracle.lse_rows(xt, s, range(a, min(a + 1024, n))) for a in range(0, n, 1024)])
+    ls = np.concatenate([oracle.lse_rows(xs, s, range(a, min(a + 1024, n))) for a in range(0, n, 1024)])
+    kl = oracle.row_kl_rows(xt, xs, s, rows)
+    dx = oracle.dx_rows(xt, xs, s, rows, lt, ls)
+    return lt, ls, kl, dx
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_full_size_sampled(gpu_lib, name):
+    import torch
+    w = si.WORKLOADS[name]
+    s = float(np.float32(w.scale))
+    maps = si.make_inputs(w)
+    rng = np.random.default_rng(100 + w.seed)
+    print(f"\n[{name}] B={w.B} n={w.n} d={w.d} heads={w.heads}", flush=True)
+    for mname, m in maps.items():
+        B, H, n, d = m.xt.shape
+        xt, xs = to_device(m.xt, w.dtype), to_device(m.xs, w.dtype)
+        ws = torch.empty(gpu_lib.workspace_bytes(B, H, n), dtype=torch.uint8, device="cuda")
+        loss, dx = gpu_lib.loss(xt, xs, w.scale, True, workspace=ws)
+        torch.cuda.synchronize()
+        off = gpu_lib.workspace_layout(B, H, n)
+        lse_t = ws[off[0]:off[0] + 8 * B * H * n].view(torch.float64).view(B, H, n)
+        lse_s = ws[off[1]:off[1] + 8 * B * H * n].view(torch.float64).view(B, H, n)
+        row_kl = ws[off[2]:off[2] + 4 * B * H * n].view(torch.float32).view(B, H, n)
+        # Any-size properties: finite outputs; KL >= -rounding; the loss is the
+        # head-summed row mean of the returned row KL.
+        assert bool(torch.isfinite(dx).all()) and bool(torch.isfinite(row_kl).all())
+        assert float(row_kl.min()) > -1e-5
+        want = float(row_kl.double().sum() / n)
+        assert abs(float(loss.cpu()) - want) <= 1e-6 * abs(want), (float(loss.cpu()), want)
+        heads = [(rng.integers(B), rng.integers(H))]
+        if n <= 8192:
+            heads.append((B - 1, H - 1))
+        for b, h in heads:
+            rows = _rows(n, rng)
+            a64, b64 = m.head64(b, h)
+            lt, ls, kl, dxr = _head_oracle(a64, b64, s, rows)
+            zmax = s * max(np.max(np.sum(a64 ** 2, 1)), np.max(np.sum(b64 ** 2, 1)))
+            g_lt = lse_t[b, h].cpu().numpy()
+            g_ls = lse_s[b, h].cpu().numpy()
+            e_lse = max(np.max(np.abs(g_lt - lt)), np.max(np.abs(g_ls - ls)))
+            g_kl = row_kl[b, h].cpu().numpy()[rows]
+            e_kl = np.max(np.abs(g_kl - kl))
+            g_dx = dx[b, h].cpu().numpy()[rows]
+            e_dx = np.max(np.abs(g_dx - dxr)) / np.max(np.abs(dxr))
+            print(f"  {mname}/{mname} head ({b},{h}): lse_err={e_lse:.2e} kl_err={e_kl:.2e} "
+                  f"dx_maxrel={e_dx:.2e} (rows={len(rows)})", flush=True)
+            assert e_lse < 2e-6 * (1 + np.max(np.abs(lt))) + 8 * EPS32 * zmax
+            assert e_kl < 2e-6 + 1e-4 * np.max(np.abs(kl)) + 8 * EPS32 * zmax
+            assert e_dx < 2e-2
+            if n <= 8192:
+                # per-head loss against the oracle's dense definition
+                full = oracle.relation_kl_head(a64, b64, s, True)["loss"]
+                got_h = float(row_kl[b, h].double().sum() / n)
+                assert abs(got_h - full) / abs(full) < 1e-3, (got_h, full)
+        del xt, xs, dx, ws
+        torch.cuda.empty_cache()

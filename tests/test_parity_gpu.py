@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: fp32 inputs 1e-5 (loss relative, gradient normwise max-relative);
+bf16 inputs 1e-3 on the loss and 2e-2 on the gradient.  LSE and per-row KL
+are compared elementwise with bounds derived from fp32 accumulation.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as si
+from helpers import normwise_max_rel, random_pair, rel, to_device, widen
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(loss=1e-5, dx=1e-5, lse=1e-9, kl=1e-7),
+       "bf16": dict(loss=1e-3, dx=2e-2, lse=2e-6, kl=2e-6)}
+EPS32 = 2.0 ** -24
+
+
+def _logit_bound(xt, xs, scale):
+    """Largest |logit| the inputs can produce: scale * max_i |x_i|^2 (Cauchy-Schwarz)."""
+    return scale * max(float(np.max(np.sum(xt ** 2, axis=-1))), float(np.max(np.sum(xs ** 2, axis=-1))))
+
+
+def f32(v: float) -> float:
+    """The scale as the C ABI receives it (a float argument); the oracle gets the same value."""
+    return float(np.float32(v))
+
+
+def _run(lmr, xt_np, xs_np, dtype, scale, causal=True, loss_scale=1.0, dx_mode=0):
+    import torch
+    xt, xs = to_device(xt_np, dtype), to_device(xs_np, dtype)
+    lse_t, lse_s = lmr.lse_fwd(xt, xs, scale, causal)
+    row_kl, dx = lmr.kl_bwd(xt, xs, lse_t, lse_s, scale, causal, loss_scale, dx_mode=dx_mode)
+    loss, dx2 = lmr.loss(xt, xs, scale, causal, loss_scale, dx_mode=dx_mode)
+    torch.cuda.synchronize()
+    out = dict(lse_t=lse_t.cpu().numpy(), lse_s=lse_s.cpu().numpy(), row_kl=row_kl.cpu().numpy(),
+               dx=dx.cpu().numpy(), loss=float(loss.cpu()), dx2=dx2.cpu().numpy())
+    return out
+
+
+def _compare(got, ref, dtype, n, zmax, loss_scale=1.0, scale=None, xmax=None):
+    """zmax: bound on |logit| (nats); fp32 logits carry an absolute error ~eps32*zmax,
+    which bounds what the LSE and per-row KL can resolve for bf16 inputs."""
+    tol = TOL[dtype]
+    scale_err = (EPS32 * zmax * 8) if dtype == "bf16" else 0.0
+    for k in ("lse_t", "lse_s"):
+        err = np.max(np.abs(got[k] - ref[k]))
+        assert err < tol["lse"] * (1 + np.max(np.abs(ref[k]))) + scale_err, (k, err)
+    kl_err = np.max(np.abs(got["row_kl"] - ref["row_kl"]))
+    assert kl_err < tol["kl"] + 1e-4 * np.max(np.abs(ref["row_kl"])) + scale_err, kl_err
+    if abs(ref["loss"]) > 1e-4 * loss_scale:
+        assert rel(got["loss"], ref["loss"]) < tol["loss"], (got["loss"], ref["loss"])
+    else:   # degenerate (near-)zero loss: absolute bound from the per-row KL bound
+        assert abs(got["loss"] - ref["loss"]) < (tol["kl"] + scale_err) * loss_scale, (got["loss"], ref["loss"])
+    e = normwise_max_rel(got["dx"], ref["dxs"])
+    if n <= 8 and dtype == "bf16":
+        # Degenerate lengths: the true gradient can be ~1e-6 of its terms, below
+        # what fp32 statistics resolve.  Each recomputed probability carries a
+        # relative error eps_p from the fp32 LSE and exp2; with at most n rows
+        # per column, |d dX| <= loss_scale*scale/n * eps_p * (2 + n) * max|x_s|.
+        eps_p = 4 * EPS32 * (1 + 1.4427 * max(np.max(np.abs(ref["lse_t"])), np.max(np.abs(ref["lse_s"]))))
+        bound = loss_scale * scale / n * eps_p * (2 + n) * xmax
+        assert e < tol["dx"] or np.max(np.abs(got["dx"] - ref["dxs"])) < bound, (e, bound)
+    else:
+        assert e < tol["dx"], e
+    # the one-call path reproduces the two-call path bit for bit
+    assert np.array_equal(got["dx"], got["dx2"])
+
+
+def test_tiny_fp32_rope_pi4(gpu_lib):
+    """Tiny fp32 Q/Q relation: n=256, d=64, PI x4 student (parity at 1e-5)."""
+    w = si.WORKLOADS["tiny_f32"]
+    m = si.make_inputs(w)["Q"]
+    got = _run(gpu_lib, m.xt, m.xs, "f32", w.scale)
+    ref = oracle.relation_kl(m.xt64, m.xs64, f32(w.scale), True)
+    _compare(got, ref, "f32", w.n, _logit_bound(m.xt64, m.xs64, w.scale))
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 333])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_ragged_lengths(gpu_lib, n, d):
+    xt, xs = random_pair(1, 2, n, d, 0.4, seed=n * 7 + d)
+    s = 1.0 / np.sqrt(d)
+    got = _run(gpu_lib, xt, xs, "bf16", s)
+    a, b = widen(xt, "bf16"), widen(xs, "bf16")
+    ref = oracle.relation_kl(a, b, f32(s), True)
+    _compare(got, ref, "bf16", n, _logit_bound(a, b, s), scale=s, xmax=float(np.max(np.abs(b))))
+
+
+@pytest.mark.parametrize("n", [1, 65, 200])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_ragged_lengths(gpu_lib, n, d):
+    xt, xs = random_pair(2, 1, n, d, 0.4, seed=n + d, dtype="f32")
+    s = 1.0 / np.sqrt(d)
+    got = _run(gpu_lib, xt, xs, "f32", s)
+    a, b = widen(xt, "f32"), widen(xs, "f32")
+    ref = oracle.relation_kl(a, b, f32(s), True)
+    _compare(got, ref, "f32", n, _logit_bound(a, b, s))
+
+
+@pytest.mark.parametrize("n,d,dtype", [(200, 128, "bf16"), (129, 64, "bf16"), (100, 64, "f32")])
+def test_bidirectional_mask(gpu_lib, n, d, dtype):
+    xt, xs = random_pair(1, 3, n, d, 0.5, seed=5, dtype=dtype)
+    s = 1.0 / np.sqrt(d)
+    got = _run(gpu_lib, xt, xs, dtype, s, causal=False)
+    a, b = widen(xt, dtype), widen(xs, dtype)
+    ref = oracle.relation_kl(a, b, f32(s), False)
+    _compare(got, ref, dtype, n, _logit_bound(a, b, s))
+
+
+def test_multi_batch_heads_and_loss_scale(gpu_lib):
+    B, H, n, d = 2, 3, 257, 128
+    xt, xs = random_pair(B, H, n, d, 0.3, seed=11)
+    s = 1.0 / np.sqrt(d)
+    ls = 1.0 / (B * H)
+    got = _run(gpu_lib, xt, xs, "bf16", s, loss_scale=ls)
+    a, b = widen(xt, "bf16"), widen(xs, "bf16")
+    ref = oracle.relation_kl(a, b, f32(s), True, loss_scale=ls)
+    _compare(got, ref, "bf16", n, _logit_bound(a, b, s), loss_scale=ls)
+
+
+def test_identical_inputs_give_exact_zero(gpu_lib):
+    xt, _ = random_pair(1, 2, 300, 128, 0.0, seed=3)
+    got = _run(gpu_lib, xt, xt.copy(), "bf16", 1 / np.sqrt(128))
+    assert got["loss"] == 0.0
+    assert np.all(got["row_kl"] == 0.0)
+    assert np.all(got["dx"] == 0.0)
+
+
+def test_single_token_and_empty(gpu_lib):
+    import torch
+    xt, xs = random_pair(1, 1, 1, 64, 1.0, seed=1)
+    got = _run(gpu_lib, xt, xs, "bf16", 0.125)
+    # One token: both rows are the single probability 1, so the exact loss and
+    # gradient are 0; what is left is fp32 rounding of exp2/log2 near 1 (KL)
+    # and of the two recomputed probabilities (gradient, relative eps_p).
+    eps_p = 4 * EPS32 * (1 + 1.4427 * float(np.max(np.abs(got["lse_t"]))))
+    assert abs(got["loss"]) < 4 * EPS32
+    assert np.max(np.abs(got["dx"])) < 0.125 * 2 * eps_p * float(np.max(np.abs(widen(xs, "bf16"))))
+    e = torch.empty((1, 1, 0, 64), dtype=torch.bfloat16, device="cuda")
+    loss, dx = gpu_lib.loss(e, e)
+    torch.cuda.synchronize()
+    assert float(loss.cpu()) == 0.0 and dx.numel() == 0
+
+
+def test_growing_logits_exercise_online_rescaling(gpu_lib):
+    # Row norms grow along the sequence, so the running max changes at every
+    # key tile and late keys dominate early ones by > 2^30.
+    n, d = 320, 64
+    rng = np.random.default_rng(8)
+    g = np.linspace(0.3, 3.0, n)[:, None]
+    xt = rng.standard_normal((1, 1, n, d)) * g
+    xs = xt + 0.2 * rng.standard_normal((1, 1, n, d)) * g
+    xt, xs = si.round_bf16_bits(xt), si.round_bf16_bits(xs)
+    got = _run(gpu_lib, xt, xs, "bf16", 0.5)
+    a, b = widen(xt, "bf16"), widen(xs, "bf16")
+    ref = oracle.relation_kl(a, b, 0.5, True)
+    _compare(got, ref, "bf16", n, _logit_bound(a, b, 0.5))
+
+
+def test_loss_only_matches_full(gpu_lib):
+    import torch
+    xt, xs = random_pair(1, 2, 190, 128, 0.3, seed=4)
+    a, b = to_device(xt, "bf16"), to_device(xs, "bf16")
+    l1, _ = gpu_lib.loss(a, b, need_dx=False)
+    l2, _ = gpu_lib.loss(a, b, need_dx=True)
+    torch.cuda.synchronize()
+    assert float(l1.cpu()) == float(l2.cpu())
+
+
+def test_split_mode_is_bitwise_deterministic(gpu_lib):
+    import torch
+    xt, xs = random_pair(1, 4, 700, 128, 0.3, seed=6)
+    a, b = to_device(xt, "bf16"), to_device(xs, "bf16")
+    outs = []
+    for _ in range(3):
+        loss, dx = gpu_lib.loss(a, b, dx_mode=gpu_lib.DX_SPLIT)
+        torch.cuda.synchronize()
+        outs.append((float(loss.cpu()), dx.cpu().numpy()))
+    for o in outs[1:]:
+        assert o[0] == outs[0][0] and np.array_equal(o[1], outs[0][1])
