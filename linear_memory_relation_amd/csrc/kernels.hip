@@ -1,4 +1,4 @@
-// gfx950 (CDNA4) kernels of the linear-memory relation-KL path.
+// gfx950 (CDNA4) kernels of the linear-memory relation-KL path, bf16 inputs.
 //
 // Method: "LinearARD: Linear-Memory Attention Distillation for RoPE
 // Restoration" (paper-notes page, section "Key designs", items 1 and 3;
@@ -9,22 +9,23 @@
 // dZ = (R_s - R_t)/n, which it contracts with the student projections.
 //
 // Tiling used by every sweep kernel in this file
-//   * A workgroup of W waves "owns" 32*W consecutive rows of one head; wave w
+//   * A workgroup of 4 waves owns 128 consecutive rows of one head; wave w
 //     owns 32 of them.  The owned rows' projections sit in registers as MFMA
 //     B operands for the whole sweep.
-//   * The other index ("swept") advances in tiles of SW rows that are staged
-//     through LDS (row-major, 16-byte XOR swizzle) and shared by all waves.
+//   * The other index ("swept") advances in tiles of 64 rows that are copied
+//     global -> LDS directly (no staging registers), double-buffered, one
+//     barrier per tile.  Each tile is processed in two 32-row sub-blocks.
 //   * Logit tiles are computed swept-major: C[swept][owned] =
 //     sum_k X[swept][k] X[owned][k] with v_mfma_f32_32x32x16_bf16, so each
-//     lane holds one owned index and 16 swept indices per 32x32 block.
-//     Row statistics therefore reduce inside a lane; a lane pair (l, l^32)
-//     is combined once at the end.
+//     lane holds one owned index and 16 swept indices per 32x32 block.  Row
+//     statistics reduce inside a lane; the lane pair (l, l^32) is combined
+//     once at the end.
 //   * The gradient contraction  out^T[d][owned] += sum_swept
 //     X_s[swept][d] * dZ'[swept][owned]  takes dZ' straight from the logit
 //     accumulators as the B operand: the 8 swept values a lane holds per
-//     16-step are exactly one B fragment under a fixed permutation of k, and
-//     the A operand X_s^T is read from a transposed LDS copy with the same
-//     permutation.
+//     16-step are one B fragment under a fixed permutation of k.  The A
+//     operand X_s^T is read from the same row-major LDS tile with the LDS
+//     transpose read (ds_read_b64_tr_b16), with the same permutation.
 //   * Row-owned sweeps (owned = query row i, swept = key j) give the row KL
 //     and the row term dZ X_s; column-owned sweeps (owned = key j, swept =
 //     row i) give the column term dZ^T X_s.  Both terms land in dX_s because
@@ -39,162 +40,197 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.69314718055994531f;
 constexpr double kLog2eD = 1.4426950408889634074;
 constexpr double kLn2D = 0.69314718055994530942;
 
-// Row statistic in log2 units split as hi + lo (hi = the fp32 rounding).
+constexpr int kW = 4;                  // waves per workgroup
+constexpr int kNT = 64 * kW;           // threads per workgroup
+constexpr int kOwn = 32 * kW;          // owned rows per workgroup
+constexpr int kSW = 64;                // swept rows per LDS tile
+
+enum : int { ROLE_ROW = 0, ROLE_COL = 1 };
+
+// Build-time tuning switches (see the tile loop of kl_sweep_kernel).
+#ifndef LMR_SWEEP_PIPE
+#define LMR_SWEEP_PIPE 0          // software-pipeline unmasked tiles
+#endif
+#ifndef LMR_SWEEP_OCC
+#define LMR_SWEEP_OCC 2           // minimum waves per SIMD the sweep is compiled for
+#endif
+#ifndef LMR_LSE_OCC
+#define LMR_LSE_OCC 2
+#endif
+
+__device__ inline f32x16 mma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline bf16x8 pack8(const float* v) {
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (__bf16)v[e];
+  return f;
+}
+
+// Row statistic in log2 units split as hi + lo (hi = its fp32 rounding).
 // Phase 2 forms exp2(z*c - hi) with one fma, exact to fp32 rounding of the
-// (small) result for the dominant entries, and applies 2^-lo as a per-row
-// factor on the probabilities that feed dZ.
+// (small) result for the dominant entries, and applies w = 2^-lo per row.
 __device__ inline void split_stat(double lse_nat, float& hi, float& w) {
   const double l2 = lse_nat * kLog2eD;
   hi = (float)l2;
   w = exp2f(-(float)(l2 - (double)hi));
 }
 
-enum : int { ROLE_ROW = 0, ROLE_COL = 1 };
-
-// ---------------------------------------------------------------------------
-// Element policies: one MFMA "k-step" consumes 16 k values; a lane in half h
-// (h = lane / 32) supplies the 8 values k = 16*ks + 8*h + e, e = 0..7.
-// ---------------------------------------------------------------------------
-template <typename T> struct Ops;
-
-template <> struct Ops<uint16_t> {           // bf16 storage (fp32 inputs use wide.hip)
-  using Frag = bf16x8;
-  using Group = bf16x4;
-  __device__ static inline f32x16 mma(const Frag& a, const Frag& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// Row-major bf16 LDS tile with 16-byte chunks XOR-swizzled by f(row).  f is
+// a bijection on 16 consecutive rows (so the 16 rows of a fragment read land
+// in 16 distinct bank groups) and maps 4 consecutive rows to 4 different
+// 4-chunk blocks (so the 4 rows x 4 chunks of a transpose read are
+// conflict free as well).
+template <int D>
+struct Tile {
+  static constexpr int RB = 2 * D;                // bytes per row
+  static constexpr int CH = RB / 16;              // chunks per row: 8 or 16
+  static constexpr int RPL = 256 / RB;            // rows per 256-byte bank line
+  static constexpr int QB = CH / 4;
+  static constexpr int QSH = QB == 4 ? 2 : 1;
+  static constexpr int BYTES = kSW * RB;
+  static_assert(D == 64 || D == 128, "head dim");
+  __device__ static inline int f(int r) {
+    const int m = r / RPL;
+    return ((m & (QB - 1)) << 2) | ((m >> QSH) & 3);
   }
-  __device__ static inline Frag pack(const float* v) {
-    Frag f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = (__bf16)v[e];
-    return f;
-  }
-  __device__ static inline Frag join(const Group& lo, const Group& hi) {
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  }
-};
-
-// Row-major LDS tile of ROWS x D elements; 16-byte chunks XOR-swizzled so the
-// 16 rows read together by a fragment load hit 16 distinct bank groups.
-template <typename T, int D>
-struct RowTile {
-  static constexpr int RB = D * (int)sizeof(T);          // bytes per row
-  static constexpr int CPR = RB / 16;                    // 16-byte chunks per row
-  static constexpr int RSH = RB >= 256 ? 0 : 1;          // 128-byte rows: two per bank line
-  static constexpr int CMASK = (CPR < 16 ? CPR : 16) - 1;
-  static_assert(RB == 128 || RB == 256, "row size");
-  __device__ static inline int off(int r, int c) { return r * RB + ((c ^ ((r >> RSH) & CMASK)) << 4); }
-  __device__ static inline typename Ops<T>::Frag frag(const char* base, int r, int ks, int h) {
+  __device__ static inline int off(int r, int c) { return r * RB + ((c ^ f(r)) << 4); }
+  // MFMA operand with k = 16*ks + 8*h + e of row r (A operand of the logits).
+  __device__ static inline bf16x8 frag(const char* base, int r, int ks, int h) {
     return *reinterpret_cast<const bf16x8*>(base + off(r, 2 * ks + h));
   }
-};
-
-// Transposed LDS copy [D][SW] of a swept tile: 4-element groups of
-// consecutive swept rows, XOR-swizzled per d so 32 lanes reading 32 d-rows
-// at the same group are conflict free.
-template <typename T, int D, int SW>
-struct ColTile {
-  static constexpr int TRB = SW * (int)sizeof(T);        // bytes per d-row
-  static constexpr int GB = 4 * (int)sizeof(T);          // bytes per group
-  static constexpr int GMASK = SW / 4 - 1;
-  static constexpr int RSH = TRB >= 256 ? 0 : 1;
-  static_assert(SW == 64, "swept tile");
-  __device__ static inline int off(int d, int g) { return d * TRB + ((g ^ ((d >> RSH) & GMASK)) * GB); }
-  // A fragment for 16-step q: swept rows 16q + 4h + 0..3 and 16q + 8 + 4h + 0..3
-  __device__ static inline typename Ops<T>::Frag frag(const char* base, int d, int q, int h) {
-    using G = typename Ops<T>::Group;
-    const G lo = *reinterpret_cast<const G*>(base + off(d, 4 * q + h));
-    const G hi = *reinterpret_cast<const G*>(base + off(d, 4 * q + 2 + h));
-    return Ops<T>::join(lo, hi);
+  // A operand X^T[d][swept] of the contraction for 16-step q and d-block db:
+  // lane (d = 32*db + lane%32, half h) gets swept rows 16q+4h+0..3 and
+  // 16q+8+4h+0..3.  In each 16-lane group G, input lane L points at row
+  // (base row + L/4) and the 4 columns 4*(L%4).. of the group's 16 columns;
+  // the transpose read hands lane 4a+b column b of rows a, a+4, a+8, a+12.
+  __device__ static inline bf16x8 tr_frag(const char* base, int q, int db, int lane) {
+    const int G = lane >> 4, L = lane & 15, h = G >> 1;
+    const int row = 16 * q + 4 * h + (L >> 2);
+    const int dcol = 32 * db + 16 * (G & 1) + 4 * (L & 3);
+    const int c = dcol >> 3, sub = (dcol & 7) * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off(row, c) + sub));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off(row + 8, c) + sub));
+    const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+    return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // Direct global -> LDS copy of kSW rows starting at row0 (rows >= n are
+  // clamped to row n-1 and masked later).  Every wave-instruction writes 1 KB
+  // of consecutive LDS (16 bytes per lane, at base + 16*lane); each lane
+  // fetches the logical chunk that the swizzle puts at its physical slot.
+  __device__ static inline void load(char* lds, const char* g, int row0, int n, int wave, int lane) {
+    constexpr int U = BYTES / 1024 / kW;          // instructions per wave
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int blk = (wave * U + u) * 1024;
+      const int P = blk + 16 * lane;
+      const int r = P / RB, pos = (P % RB) >> 4;
+      const int c = pos ^ f(r);
+      const int gr = min(row0 + r, n - 1);
+      const char* src = g + (int64_t)gr * RB + 16 * c;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(lds + blk), 16, 0, 0);
+    }
   }
 };
 
-// Owned-row fragment straight from global memory (row pointer may be null = zeros).
-template <typename T>
-__device__ inline typename Ops<T>::Frag load_own(const char* row, int ks, int h) {
-  using F = typename Ops<T>::Frag;
-  if (row == nullptr) return F{};
-  return *reinterpret_cast<const bf16x8*>(row + (16 * ks + 8 * h) * (int)sizeof(T));
+__device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Owned-row MFMA B operand straight from global memory (null row = zeros).
+__device__ inline bf16x8 load_own(const char* row, int ks, int h) {
+  if (row == nullptr) return bf16x8{};
+  return *reinterpret_cast<const bf16x8*>(row + (16 * ks + 8 * h) * 2);
 }
 
-// Global -> registers -> LDS staging of one swept tile of X_t and X_s.
-template <typename T, int D, int SW, int NT>
-struct Stager {
-  static constexpr int RB = D * (int)sizeof(T);
-  static constexpr int CPR = RB / 16;
-  static constexpr int CPT = SW * CPR / NT;               // chunks per thread per matrix
-  static constexpr int EPC = 16 / (int)sizeof(T);         // elements per chunk
-  static_assert(SW * CPR % NT == 0, "staging split");
-  uint4 t[CPT], s[CPT];
-
-  __device__ inline void load(const char* xt, const char* xs, int row0, int n, int tid) {
+// Both 32x32 logit blocks of swept sub-block sb against the wave's owned rows.
+template <int D>
+__device__ inline void logits(const char* lt, const char* ls, const bf16x8* Bt, const bf16x8* Bs,
+                              f32x16& St, f32x16& Ss, int sb, int lane) {
+  constexpr int KS = D / 16;
+  const int h = lane >> 5, rr = 32 * sb + (lane & 31);
+  St = f32x16{};
+  Ss = f32x16{};
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int q = tid + NT * u, r = q / CPR, c = q % CPR, g = row0 + r;
-      if (g < n) {
-        t[u] = *reinterpret_cast<const uint4*>(xt + (int64_t)g * RB + c * 16);
-        s[u] = *reinterpret_cast<const uint4*>(xs + (int64_t)g * RB + c * 16);
-      } else {
-        t[u] = make_uint4(0, 0, 0, 0);
-        s[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-  __device__ inline void store(char* lt, char* ls, char* lsT, int tid) const {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int q = tid + NT * u, r = q / CPR, c = q % CPR;
-      *reinterpret_cast<uint4*>(lt + RowTile<T, D>::off(r, c)) = t[u];
-      *reinterpret_cast<uint4*>(ls + RowTile<T, D>::off(r, c)) = s[u];
-      if (lsT != nullptr) {
-        const T* e = reinterpret_cast<const T*>(&s[u]);
-#pragma unroll
-        for (int k = 0; k < EPC; ++k)
-          *reinterpret_cast<T*>(lsT + ColTile<T, D, SW>::off(c * EPC + k, r >> 2) + (r & 3) * (int)sizeof(T)) = e[k];
-      }
-    }
-  }
-};
-
-// Both logit tiles of one swept LDS tile against the wave's owned rows.
-template <typename T, int D, int SW>
-__device__ inline void logits(const char* lt, const char* ls, const typename Ops<T>::Frag* Bt,
-                              const typename Ops<T>::Frag* Bs, f32x16* St, f32x16* Ss, int lane) {
-  constexpr int KS = D / 16, MB = SW / 32;
-  const int h = lane >> 5, rr = lane & 31;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    St[mb] = f32x16{};
-    Ss[mb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      St[mb] = Ops<T>::mma(RowTile<T, D>::frag(lt, 32 * mb + rr, ks, h), Bt[ks], St[mb]);
-      Ss[mb] = Ops<T>::mma(RowTile<T, D>::frag(ls, 32 * mb + rr, ks, h), Bs[ks], Ss[mb]);
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    St = mma(Tile<D>::frag(lt, rr, ks, h), Bt[ks], St);
+    Ss = mma(Tile<D>::frag(ls, rr, ks, h), Bs[ks], Ss);
   }
 }
 
-// Swept offset (within a tile) of accumulator element r of block mb for lane half h.
-__device__ inline int swept_of(int mb, int r, int h) { return 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3); }
+// Gradient contraction of sub-block sb: acc[db] (out^T[d][owned]) +=
+// X_s^T[d][swept] * dZ'[swept][owned], dZ' taken from the logit registers.
+template <int D>
+__device__ inline void contract(const f32x16& dz, const char* ls, int sb, int lane, f32x16* acc) {
+  constexpr int DB = D / 32;
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = dz[8 * q2 + e];
+    const bf16x8 bdz = pack8(v);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = mma(Tile<D>::tr_frag(ls, 2 * sb + q2, db, lane), bdz, acc[db]);
+  }
+}
+
+// Swept offset within a 32-row block of accumulator element r for half h.
+__device__ inline int swept_of(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
 // ---------------------------------------------------------------------------
 // Phase 1: per-row LSE of teacher and student (row-owned sweep).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int W, int SW>
-__global__ __launch_bounds__(W * 64) void lse_fwd_kernel(SweepArgs a, int nblk) {
-  constexpr int NT = W * 64, OWN = 32 * W, KS = D / 16, MB = SW / 32;
-  constexpr int RB = D * (int)sizeof(T);
-  using Frag = typename Ops<T>::Frag;
-  __shared__ __attribute__((aligned(16))) char lt[SW * RB];
-  __shared__ __attribute__((aligned(16))) char ls[SW * RB];
+// Running sums are fp64: a row of 32K keys adds ~1000 block sums into each
+// lane's total, and fp32 would let that error reach ~1e-4 of the LSE.
+template <bool MASK>
+__device__ inline void lse_block(const f32x16& St, const f32x16& Ss, float c, int sw_base, int i, int n,
+                                 int causal, int h, float& mt, double& lt, float& ms, double& ls) {
+  float zt[16], zs[16];
+  float tmt = -INFINITY, tms = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    zt[r] = St[r];
+    zs[r] = Ss[r];
+    if (MASK) {
+      const int j = sw_base + swept_of(r, h);
+      const bool ok = (!causal || j <= i) && j < n;
+      zt[r] = ok ? zt[r] : -INFINITY;
+      zs[r] = ok ? zs[r] : -INFINITY;
+    }
+    tmt = fmaxf(tmt, zt[r]);
+    tms = fmaxf(tms, zs[r]);
+  }
+  const float mnt = fmaxf(mt, tmt), mns = fmaxf(ms, tms);
+  const float mct = mnt == -INFINITY ? 0.f : mnt * c;
+  const float mcs = mns == -INFINITY ? 0.f : mns * c;
+  float at = 0.f, as = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    at += __builtin_amdgcn_exp2f(fmaf(zt[r], c, -mct));
+    as += __builtin_amdgcn_exp2f(fmaf(zs[r], c, -mcs));
+  }
+  if (mnt != mt) lt *= (double)__builtin_amdgcn_exp2f(fmaf(mt, c, -mct));
+  if (mns != ms) ls *= (double)__builtin_amdgcn_exp2f(fmaf(ms, c, -mcs));
+  lt += (double)at;
+  ls += (double)as;
+  mt = mnt;
+  ms = mns;
+}
+
+template <int D>
+__global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, int nblk) {
+  constexpr int KS = D / 16, RB = 2 * D, TB = Tile<D>::BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][TB];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
   const int64_t bid = blockIdx.x;
@@ -203,78 +239,58 @@ __global__ __launch_bounds__(W * 64) void lse_fwd_kernel(SweepArgs a, int nblk) 
   const int n = a.n;
   const char* xt = static_cast<const char*>(a.xt) + bh * (int64_t)n * RB;
   const char* xs = static_cast<const char*>(a.xs) + bh * (int64_t)n * RB;
-  const int own0 = ob * OWN, wown0 = own0 + 32 * wave, i = wown0 + (lane & 31);
+  const int own0 = ob * kOwn, wown0 = own0 + 32 * wave, i = wown0 + (lane & 31);
 
-  Frag Bt[KS], Bs[KS];
+  bf16x8 Bt[KS], Bs[KS];
   {
     const char* rt = i < n ? xt + (int64_t)i * RB : nullptr;
     const char* rs = i < n ? xs + (int64_t)i * RB : nullptr;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) { Bt[ks] = load_own<T>(rt, ks, h); Bs[ks] = load_own<T>(rs, ks, h); }
+    for (int ks = 0; ks < KS; ++ks) { Bt[ks] = load_own(rt, ks, h); Bs[ks] = load_own(rs, ks, h); }
   }
-  const int last = a.causal ? min(own0 + OWN, n) - 1 : n - 1;
-  const int ntiles = last / SW + 1;
+  const int last = a.causal ? min(own0 + kOwn, n) - 1 : n - 1;
+  const int ntiles = last / kSW + 1;
   const float c = a.scale * kLog2e;
-  float mt = -INFINITY, lsum_t = 0.f, ms = -INFINITY, lsum_s = 0.f;
+  float mt = -INFINITY, ms = -INFINITY;
+  double lsum_t = 0.0, lsum_s = 0.0;
 
-  Stager<T, D, SW, NT> stg;
-  stg.load(xt, xs, 0, n, tid);
+  Tile<D>::load(lds[0][0], xt, 0, n, wave, lane);
+  Tile<D>::load(lds[0][1], xs, 0, n, wave, lane);
   for (int tI = 0; tI < ntiles; ++tI) {
-    const int sw0 = tI * SW;
+    const int buf = tI & 1, sw0 = tI * kSW;
+    wait_loads();
     __syncthreads();
-    stg.store(lt, ls, nullptr, tid);
-    __syncthreads();
-    if (tI + 1 < ntiles) stg.load(xt, xs, sw0 + SW, n, tid);
+    if (tI + 1 < ntiles) {
+      Tile<D>::load(lds[buf ^ 1][0], xt, sw0 + kSW, n, wave, lane);
+      Tile<D>::load(lds[buf ^ 1][1], xs, sw0 + kSW, n, wave, lane);
+    }
     if (a.causal && sw0 > wown0 + 31) continue;          // tile fully above the diagonal
-    const bool need_mask = (a.causal && sw0 + SW - 1 > wown0) || (sw0 + SW > n);
-
-    f32x16 St[MB], Ss[MB];
-    logits<T, D, SW>(lt, ls, Bt, Bs, St, Ss, lane);
-    float tmt = -INFINITY, tms = -INFINITY;
+    const bool need_mask = (a.causal && sw0 + kSW - 1 > wown0) || (sw0 + kSW > n);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (need_mask) {
-          const int j = sw0 + swept_of(mb, r, h);
-          const bool ok = (!a.causal || j <= i) && j < n;
-          St[mb][r] = ok ? St[mb][r] : -INFINITY;
-          Ss[mb][r] = ok ? Ss[mb][r] : -INFINITY;
-        }
-        tmt = fmaxf(tmt, St[mb][r]);
-        tms = fmaxf(tms, Ss[mb][r]);
-      }
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x16 St, Ss;
+      logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
+      if (need_mask)
+        lse_block<true>(St, Ss, c, sw0 + 32 * sb, i, n, a.causal, h, mt, lsum_t, ms, lsum_s);
+      else
+        lse_block<false>(St, Ss, c, sw0 + 32 * sb, i, n, a.causal, h, mt, lsum_t, ms, lsum_s);
     }
-    const float mnt = fmaxf(mt, tmt), mns = fmaxf(ms, tms);
-    const float mct = mnt == -INFINITY ? 0.f : mnt * c;
-    const float mcs = mns == -INFINITY ? 0.f : mns * c;
-    float at = 0.f, as = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        at += __builtin_amdgcn_exp2f(fmaf(St[mb][r], c, -mct));
-        as += __builtin_amdgcn_exp2f(fmaf(Ss[mb][r], c, -mcs));
-      }
-    }
-    lsum_t = lsum_t * __builtin_amdgcn_exp2f(fmaf(mt, c, -mct)) + at;
-    lsum_s = lsum_s * __builtin_amdgcn_exp2f(fmaf(ms, c, -mcs)) + as;
-    mt = mnt;
-    ms = mns;
   }
   // Combine the two lane halves that share owned row i.
-  const float mt2 = __shfl_xor(mt, 32), lt2 = __shfl_xor(lsum_t, 32);
-  const float ms2 = __shfl_xor(ms, 32), ls2 = __shfl_xor(lsum_s, 32);
+  const float mt2 = __shfl_xor(mt, 32), ms2 = __shfl_xor(ms, 32);
+  const double lt2 = __shfl_xor(lsum_t, 32), ls2 = __shfl_xor(lsum_s, 32);
   const float Mt = fmaxf(mt, mt2), Ms = fmaxf(ms, ms2);
   const float Mct = Mt * c, Mcs = Ms * c;
-  const float Lt = lsum_t * __builtin_amdgcn_exp2f(fmaf(mt, c, -Mct)) + lt2 * __builtin_amdgcn_exp2f(fmaf(mt2, c, -Mct));
-  const float Ls = lsum_s * __builtin_amdgcn_exp2f(fmaf(ms, c, -Mcs)) + ls2 * __builtin_amdgcn_exp2f(fmaf(ms2, c, -Mcs));
+  // The shifts Mt*c are exact fp32 values; exp2 of their (small) differences
+  // is evaluated in fp64 so the combination adds no fp32 rounding.
+  const double Lt = lsum_t * exp2((double)fmaf(mt, c, -Mct)) + lt2 * exp2((double)fmaf(mt2, c, -Mct));
+  const double Ls = lsum_s * exp2((double)fmaf(ms, c, -Mcs)) + ls2 * exp2((double)fmaf(ms2, c, -Mcs));
   // LSE = ln2 * (M*c + log2 L), assembled in fp64 from the fp32 shift that
   // the exponentials above actually used, so the stored statistic carries no
   // rounding of M*c.
   if (h == 0 && i < n) {
-    static_cast<double*>(a.lse_t)[bh * n + i] = ((double)Mct + (double)log2f(Lt)) * kLn2D;
-    static_cast<double*>(a.lse_s)[bh * n + i] = ((double)Mcs + (double)log2f(Ls)) * kLn2D;
+    static_cast<double*>(a.lse_t)[bh * n + i] = ((double)Mct + log2(Lt)) * kLn2D;
+    static_cast<double*>(a.lse_s)[bh * n + i] = ((double)Mcs + log2(Ls)) * kLn2D;
   }
 }
 
@@ -299,16 +315,78 @@ __global__ __launch_bounds__(W * 64) void lse_fwd_kernel(SweepArgs a, int nblk) 
 // sweep forms (p_s - p_t * w_t/w_s) * w_s per entry.  Identical teacher and
 // student inputs therefore give exactly zero.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int W, int SW, int ROLE, bool WITH_DX>
-__global__ __launch_bounds__(W * 64) void kl_sweep_kernel(SweepArgs a, int nblk) {
-  constexpr int NT = W * 64, OWN = 32 * W, KS = D / 16, MB = SW / 32, DB = D / 32;
-  constexpr int RB = D * (int)sizeof(T);
-  using Frag = typename Ops<T>::Frag;
-  __shared__ __attribute__((aligned(16))) char lt[SW * RB];
-  __shared__ __attribute__((aligned(16))) char ls[SW * RB];
-  __shared__ __attribute__((aligned(16))) char lsT[WITH_DX ? D * SW * (int)sizeof(T) : 16];
-  // COL: per swept row hi_t, hi_s, w_t/w_s, w_s (see split_stat)
-  __shared__ __attribute__((aligned(16))) float llse[ROLE == ROLE_COL ? 4 * SW : 4];
+
+// Per-lane running state of a row sweep: per-block fp32 partials are added
+// into fp64 totals (rows of 32K keys add ~1000 blocks per lane).
+struct SweepState {
+  double kl = 0.0, off_t = 0.0, off_s = 0.0;
+  float pd_t = 0.f, pd_s = 0.f;
+};
+
+// Elementwise step on one 32x32 block, in place: St <- dZ * n.
+// SPECIAL: the block may hold masked or diagonal entries of this wave.
+template <int ROLE, bool SPECIAL>
+__device__ inline void block_elementwise(f32x16& St, const f32x16& Ss, float c, int sw_base, int o, int n,
+                                         int causal, int h, float l2t, float l2s, float wts,
+                                         const float4* stat, SweepState& S) {
+  float kl = 0.f, off_t = 0.f, off_s = 0.f;
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g4 + e;
+      float bt = l2t, bs = l2s, rr = wts, wsr = 1.f;
+      if (ROLE == ROLE_COL) {
+        const float4 st = stat[8 * g4 + 4 * h + e];
+        bt = st.x;
+        bs = st.y;
+        rr = st.z;
+        wsr = st.w;
+      }
+      float at = fmaf(St[r], c, -bt);
+      float as = fmaf(Ss[r], c, -bs);
+      float pt = __builtin_amdgcn_exp2f(at);
+      float ps = __builtin_amdgcn_exp2f(as);
+      bool offdiag = true;
+      if (SPECIAL) {
+        const int sw = sw_base + swept_of(r, h);
+        const int ii = ROLE == ROLE_ROW ? o : sw;
+        const int jj = ROLE == ROLE_ROW ? sw : o;
+        const bool ok = (!causal || jj <= ii) && sw < n;
+        const bool diag = ok && sw == o;
+        pt = ok ? pt : 0.f;
+        ps = ok ? ps : 0.f;
+        at = ok ? at : 0.f;
+        as = ok ? as : 0.f;
+        if (ROLE == ROLE_ROW) {
+          S.pd_t = diag ? pt : S.pd_t;
+          S.pd_s = diag ? ps : S.pd_s;
+        }
+        offdiag = !diag;
+      }
+      if (ROLE == ROLE_ROW) {
+        kl = fmaf(pt, at - as, kl);
+        off_t += offdiag ? pt : 0.f;
+        off_s += offdiag ? ps : 0.f;
+      }
+      const float dz = ROLE == ROLE_ROW ? fmaf(-pt, rr, ps) : fmaf(-pt, rr, ps) * wsr;
+      St[r] = offdiag ? dz : 0.f;
+    }
+  }
+  if (ROLE == ROLE_ROW) {
+    S.kl += (double)kl;
+    S.off_t += (double)off_t;
+    S.off_s += (double)off_s;
+  }
+}
+
+template <int D, int ROLE, bool WITH_DX>
+__global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs a, int nblk) {
+  constexpr int KS = D / 16, DB = D / 32, RB = 2 * D, TB = Tile<D>::BYTES;
+  constexpr int NSTAT = ROLE == ROLE_COL ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][TB];
+  // COL: per swept row (hi_t, hi_s, w_t/w_s, w_s), double-buffered.
+  __shared__ float4 lstat[NSTAT][ROLE == ROLE_COL ? kSW : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
   const int64_t bid = blockIdx.x;
@@ -317,155 +395,145 @@ __global__ __launch_bounds__(W * 64) void kl_sweep_kernel(SweepArgs a, int nblk)
   const int n = a.n;
   const char* xt = static_cast<const char*>(a.xt) + bh * (int64_t)n * RB;
   const char* xs = static_cast<const char*>(a.xs) + bh * (int64_t)n * RB;
-  const int own0 = ob * OWN, wown0 = own0 + 32 * wave, o = wown0 + (lane & 31);
+  const double* glt = static_cast<const double*>(a.lse_t) + bh * n;
+  const double* gls = static_cast<const double*>(a.lse_s) + bh * n;
+  const int own0 = ob * kOwn, wown0 = own0 + 32 * wave, o = wown0 + (lane & 31);
   const float c = a.scale * kLog2e;
 
-  Frag Bt[KS], Bs[KS];
+  bf16x8 Bt[KS], Bs[KS];
   {
     const char* rt = o < n ? xt + (int64_t)o * RB : nullptr;
     const char* rs = o < n ? xs + (int64_t)o * RB : nullptr;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) { Bt[ks] = load_own<T>(rt, ks, h); Bs[ks] = load_own<T>(rs, ks, h); }
+    for (int ks = 0; ks < KS; ++ks) { Bt[ks] = load_own(rt, ks, h); Bs[ks] = load_own(rs, ks, h); }
   }
   float l2t = 0.f, l2s = 0.f, wts = 1.f, ws = 1.f;      // owned-row statistics (ROW)
   if (ROLE == ROLE_ROW && o < n) {
     float wt;
-    split_stat(static_cast<const double*>(a.lse_t)[bh * n + o], l2t, wt);
-    split_stat(static_cast<const double*>(a.lse_s)[bh * n + o], l2s, ws);
+    split_stat(glt[o], l2t, wt);
+    split_stat(gls[o], l2s, ws);
     wts = wt / ws;
   }
   int t_begin, t_end;
   if (ROLE == ROLE_ROW) {
     t_begin = 0;
-    t_end = (a.causal ? min(own0 + OWN, n) - 1 : n - 1) / SW + 1;
+    t_end = (a.causal ? min(own0 + kOwn, n) - 1 : n - 1) / kSW + 1;
   } else {
-    t_begin = a.causal ? own0 / SW : 0;
-    t_end = (n - 1) / SW + 1;
+    t_begin = a.causal ? own0 / kSW : 0;
+    t_end = (n - 1) / kSW + 1;
   }
 
-  // Row KL in log2 units, accumulated against the stored statistics and
-  // renormalised at the end by the row sums of both probability rows, so a
-  // rounding error of a stored LSE (a constant shift of the row) cancels.
-  // off_t/off_s: off-diagonal probability sums; pd_t/pd_s: diagonal ones.
-  float kl = 0.f, off_t = 0.f, off_s = 0.f, pd_t = 0.f, pd_s = 0.f;
+  SweepState S;
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  Stager<T, D, SW, NT> stg;
-  stg.load(xt, xs, t_begin * SW, n, tid);
-  for (int tI = t_begin; tI < t_end; ++tI) {
-    const int sw0 = tI * SW;
-    __syncthreads();
-    stg.store(lt, ls, WITH_DX ? lsT : nullptr, tid);
-    if (ROLE == ROLE_COL && tid < SW) {
-      const int g = sw0 + tid;
-      float ht = 0.f, hs = 0.f, ft = 1.f, fs = 1.f;
-      if (g < n) {
-        split_stat(static_cast<const double*>(a.lse_t)[bh * n + g], ht, ft);
-        split_stat(static_cast<const double*>(a.lse_s)[bh * n + g], hs, fs);
-      }
-      llse[tid] = ht;
-      llse[SW + tid] = hs;
-      llse[2 * SW + tid] = ft / fs;
-      llse[3 * SW + tid] = fs;
+  // COL statistics: threads 0..63 hold the fp64 LSE of the next tile's rows.
+  double nlt = 0.0, nls = 0.0;
+  auto fetch_stat = [&](int tile) {
+    const int g = tile * kSW + tid;
+    nlt = g < n ? glt[g] : 0.0;
+    nls = g < n ? gls[g] : 0.0;
+  };
+  auto put_stat = [&](int b, int tile) {
+    const int g = tile * kSW + tid;
+    float ht = 0.f, hs = 0.f, ft = 1.f, fs = 1.f;
+    if (g < n) {
+      split_stat(nlt, ht, ft);
+      split_stat(nls, hs, fs);
     }
+    lstat[b][tid] = make_float4(ht, hs, ft / fs, fs);
+  };
+
+  Tile<D>::load(lds[0][0], xt, t_begin * kSW, n, wave, lane);
+  Tile<D>::load(lds[0][1], xs, t_begin * kSW, n, wave, lane);
+  if (ROLE == ROLE_COL && tid < kSW) {
+    fetch_stat(t_begin);
+    put_stat(0, t_begin);
+    if (t_begin + 1 < t_end) fetch_stat(t_begin + 1);
+  }
+  for (int tI = t_begin; tI < t_end; ++tI) {
+    const int buf = (tI - t_begin) & 1, sw0 = tI * kSW;
+    wait_loads();
     __syncthreads();
-    if (tI + 1 < t_end) stg.load(xt, xs, sw0 + SW, n, tid);
+    if (tI + 1 < t_end) {
+      Tile<D>::load(lds[buf ^ 1][0], xt, sw0 + kSW, n, wave, lane);
+      Tile<D>::load(lds[buf ^ 1][1], xs, sw0 + kSW, n, wave, lane);
+      if (ROLE == ROLE_COL && tid < kSW) {
+        put_stat(buf ^ 1, tI + 1);
+        if (tI + 2 < t_end) fetch_stat(tI + 2);
+      }
+    }
     bool skip, need_mask;
     if (ROLE == ROLE_ROW) {
       skip = a.causal && sw0 > wown0 + 31;
-      need_mask = (a.causal && sw0 + SW - 1 > wown0) || (sw0 + SW > n);
+      need_mask = (a.causal && sw0 + kSW - 1 > wown0) || (sw0 + kSW > n);
     } else {
-      skip = a.causal && wown0 > sw0 + SW - 1;
-      need_mask = (a.causal && wown0 + 31 > sw0) || (sw0 + SW > n);
+      skip = a.causal && wown0 > sw0 + kSW - 1;
+      need_mask = (a.causal && wown0 + 31 > sw0) || (sw0 + kSW > n);
     }
     if (skip) continue;
     // Tiles that hold a diagonal entry of this wave take the per-entry path too.
-    const bool special = need_mask || (sw0 <= wown0 + 31 && sw0 + SW - 1 >= wown0);
-
-    f32x16 St[MB], Ss[MB];
-    logits<T, D, SW>(lt, ls, Bt, Bs, St, Ss, lane);
+    const bool special = need_mask || (sw0 <= wown0 + 31 && sw0 + kSW - 1 >= wown0);
+    const char* lt = lds[buf][0];
+    const char* ls = lds[buf][1];
+    const float4* stat0 = &lstat[ROLE == ROLE_COL ? buf : 0][0];
+    const float4* stat1 = &lstat[ROLE == ROLE_COL ? buf : 0][ROLE == ROLE_COL ? 32 : 0];
+    if (LMR_SWEEP_PIPE && !special) {
+      // Software pipeline over the two sub-blocks: the logit MFMAs of
+      // sub-block 1 run under the elementwise work of sub-block 0, and the
+      // contraction MFMAs of sub-block 0 under the elementwise work of 1.
+      f32x16 St0, Ss0, St1, Ss1;
+      logits<D>(lt, ls, Bt, Bs, St0, Ss0, 0, lane);
+      logits<D>(lt, ls, Bt, Bs, St1, Ss1, 1, lane);
+      block_elementwise<ROLE, false>(St0, Ss0, c, sw0, o, n, a.causal, h, l2t, l2s, wts, stat0, S);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 lt4, ls4, rr4, ws4;
-        if (ROLE == ROLE_COL) {
-          const int rr = 32 * mb + 8 * g4 + 4 * h;
-          lt4 = *reinterpret_cast<const f32x4*>(&llse[rr]);
-          ls4 = *reinterpret_cast<const f32x4*>(&llse[SW + rr]);
-          rr4 = *reinterpret_cast<const f32x4*>(&llse[2 * SW + rr]);
-          ws4 = *reinterpret_cast<const f32x4*>(&llse[3 * SW + rr]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          const float bt = ROLE == ROLE_ROW ? l2t : lt4[e];
-          const float bs = ROLE == ROLE_ROW ? l2s : ls4[e];
-          float at = fmaf(St[mb][r], c, -bt);
-          float as = fmaf(Ss[mb][r], c, -bs);
-          float pt = __builtin_amdgcn_exp2f(at);
-          float ps = __builtin_amdgcn_exp2f(as);
-          bool offdiag = true;
-          if (special) {
-            const int sw = sw0 + swept_of(mb, r, h);
-            const int ii = ROLE == ROLE_ROW ? o : sw;
-            const int jj = ROLE == ROLE_ROW ? sw : o;
-            const bool ok = (!a.causal || jj <= ii) && sw < n;
-            const bool diag = ok && sw == o;
-            pt = ok ? pt : 0.f;
-            ps = ok ? ps : 0.f;
-            at = ok ? at : 0.f;
-            as = ok ? as : 0.f;
-            if (ROLE == ROLE_ROW) {
-              pd_t = diag ? pt : pd_t;
-              pd_s = diag ? ps : pd_s;
-            }
-            offdiag = !diag;
-          }
-          if (ROLE == ROLE_ROW) {
-            kl = fmaf(pt, at - as, kl);
-            off_t += offdiag ? pt : 0.f;
-            off_s += offdiag ? ps : 0.f;
-          }
-          // dZ * n in place (see the kernel comment for the 2^-lo factors).
-          float dz = ROLE == ROLE_ROW ? fmaf(-pt, wts, ps) : fmaf(-pt, rr4[e], ps) * ws4[e];
-          St[mb][r] = offdiag ? dz : 0.f;
-        }
+      for (int k = 0; k < 2 * KS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // then VALU
       }
-    }
-    if constexpr (WITH_DX) {
+      if constexpr (WITH_DX) contract<D>(St0, ls, 0, lane, acc);
+      block_elementwise<ROLE, false>(St1, Ss1, c, sw0 + 32, o, n, a.causal, h, l2t, l2s, wts, stat1, S);
+      if constexpr (WITH_DX) {
 #pragma unroll
-      for (int q = 0; q < SW / 16; ++q) {
-        float v[8];
+        for (int k = 0; k < 2 * DB; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        }
+        contract<D>(St1, ls, 1, lane, acc);
+      }
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = St[q >> 1][8 * (q & 1) + e];
-        const Frag bdz = Ops<T>::pack(v);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          acc[db] = Ops<T>::mma(ColTile<T, D, SW>::frag(lsT, 32 * db + (lane & 31), q, h), bdz, acc[db]);
+      for (int sb = 0; sb < 2; ++sb) {
+        f32x16 St, Ss;
+        logits<D>(lt, ls, Bt, Bs, St, Ss, sb, lane);
+        const float4* stat = sb ? stat1 : stat0;
+        if (special)
+          block_elementwise<ROLE, true>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, wts, stat, S);
+        else
+          block_elementwise<ROLE, false>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, wts, stat, S);
+        if constexpr (WITH_DX) contract<D>(St, ls, sb, lane, acc);
       }
     }
   }
 
   float corr = 0.f;                                      // ROW: -2 * sum_{j!=i} dZ(i,j) / w_s(i) * n
   if (ROLE == ROLE_ROW) {
-    kl += __shfl_xor(kl, 32);
-    off_t += __shfl_xor(off_t, 32);
-    off_s += __shfl_xor(off_s, 32);
-    pd_t += __shfl_xor(pd_t, 32);
-    pd_s += __shfl_xor(pd_s, 32);
-    const float sum_t = off_t + pd_t, sum_s = off_s + pd_s;
+    S.kl += __shfl_xor(S.kl, 32);
+    S.off_t += __shfl_xor(S.off_t, 32);
+    S.off_s += __shfl_xor(S.off_s, 32);
+    S.pd_t += __shfl_xor(S.pd_t, 32);
+    S.pd_s += __shfl_xor(S.pd_s, 32);
+    const double sum_t = S.off_t + (double)S.pd_t, sum_s = S.off_s + (double)S.pd_s;
     // KL = sum_j r_t (log2 r_t - log2 r_s) ln2 with r = p / sum p.
-    const float klr = kl / sum_t - log2f(sum_t) + log2f(sum_s);
-    if (h == 0 && o < n && a.row_kl != nullptr) a.row_kl[bh * n + o] = klr * kLn2;
-    corr = -2.f * fmaf(-off_t, wts, off_s);
+    const double klr = S.kl / sum_t - log2(sum_t) + log2(sum_s);
+    if (h == 0 && o < n && a.row_kl != nullptr) a.row_kl[bh * n + o] = (float)(klr * kLn2D);
+    corr = (float)(-2.0 * (S.off_s - S.off_t * (double)wts));
   }
   if constexpr (WITH_DX) {
     if (o < n) {
       float* dst = a.dx + (bh * (int64_t)n + o) * D;
-      const T* xo = reinterpret_cast<const T*>(xs + (int64_t)o * RB);
+      const uint16_t* xo = reinterpret_cast<const uint16_t*>(xs + (int64_t)o * RB);
       const float gs = ROLE == ROLE_ROW ? a.grad_scale * ws : a.grad_scale;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -532,27 +600,23 @@ __global__ void zero_scalar_kernel(float* p) { *p = 0.f; }
 // ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
-constexpr int kW = 4;       // waves per workgroup
-constexpr int kSW = 64;     // swept tile rows
-constexpr int kOwn = 32 * kW;
-
 inline int blocks_per_head(int n) { return (n + kOwn - 1) / kOwn; }
 
-template <typename T, int D>
+template <int D>
 hipError_t lse_typed(const SweepArgs& a, hipStream_t st) {
   const int nb = blocks_per_head(a.n);
-  hipLaunchKernelGGL((lse_fwd_kernel<T, D, kW, kSW>), dim3((unsigned)(nb * a.bh)), dim3(64 * kW), 0, st, a, nb);
+  hipLaunchKernelGGL((lse_fwd_kernel<D>), dim3((unsigned)(nb * a.bh)), dim3(kNT), 0, st, a, nb);
   return hipGetLastError();
 }
 
-template <typename T, int D, int ROLE>
+template <int D, int ROLE>
 hipError_t sweep_typed(const SweepArgs& a, hipStream_t st) {
   const int nb = blocks_per_head(a.n);
-  const dim3 grid((unsigned)(nb * a.bh)), block(64 * kW);
+  const dim3 grid((unsigned)(nb * a.bh)), block(kNT);
   if (a.dx != nullptr)
-    hipLaunchKernelGGL((kl_sweep_kernel<T, D, kW, kSW, ROLE, true>), grid, block, 0, st, a, nb);
+    hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, true>), grid, block, 0, st, a, nb);
   else
-    hipLaunchKernelGGL((kl_sweep_kernel<T, D, kW, kSW, ROLE, false>), grid, block, 0, st, a, nb);
+    hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, false>), grid, block, 0, st, a, nb);
   return hipGetLastError();
 }
 
@@ -560,17 +624,19 @@ hipError_t sweep_typed(const SweepArgs& a, hipStream_t st) {
 
 hipError_t launch_lse_fwd(const SweepArgs& a, hipStream_t st) {
   if (a.fp32) return launch_wide_lse_fwd(a, st);
-  return a.d == 64 ? lse_typed<uint16_t, 64>(a, st) : lse_typed<uint16_t, 128>(a, st);
+  return a.d == 64 ? lse_typed<64>(a, st) : lse_typed<128>(a, st);
 }
 
 hipError_t launch_kl_row(const SweepArgs& a, hipStream_t st) {
   if (a.fp32) return launch_wide_kl_row(a, st);
-  return a.d == 64 ? sweep_typed<uint16_t, 64, ROLE_ROW>(a, st) : sweep_typed<uint16_t, 128, ROLE_ROW>(a, st);
+  return a.d == 64 ? sweep_typed<64, ROLE_ROW>(a, st) : sweep_typed<128, ROLE_ROW>(a, st);
 }
 
 hipError_t launch_kl_col(const SweepArgs& a, hipStream_t st) {
   if (a.fp32) return launch_wide_kl_col(a, st);
-  return a.d == 64 ? sweep_typed<uint16_t, 64, ROLE_COL>(a, st) : sweep_typed<uint16_t, 128, ROLE_COL>(a, st);
+  // The column term only exists with a gradient; without one there is nothing to do.
+  if (a.dx == nullptr) return hipSuccess;
+  return a.d == 64 ? sweep_typed<64, ROLE_COL>(a, st) : sweep_typed<128, ROLE_COL>(a, st);
 }
 
 hipError_t launch_reduce(const float* row_kl, int64_t bh, int n, float loss_scale, double* partials,
