@@ -63,6 +63,12 @@ enum : int { ROLE_ROW = 0, ROLE_COL = 1 };
 #ifndef LMR_SWEEP_OCC
 #define LMR_SWEEP_OCC 2           // minimum waves per SIMD the sweep is compiled for
 #endif
+#ifndef LMR_PIPE_V1
+#define LMR_PIPE_V1 10            // VALU instructions per logit MFMA in the pipeline
+#endif
+#ifndef LMR_PIPE_V2
+#define LMR_PIPE_V2 20            // VALU instructions per contraction MFMA
+#endif
 #ifndef LMR_LSE_OCC
 #define LMR_LSE_OCC 2
 #endif
@@ -80,11 +86,11 @@ __device__ inline bf16x8 pack8(const float* v) {
 
 // Row statistic in log2 units split as hi + lo (hi = its fp32 rounding).
 // Phase 2 forms exp2(z*c - hi) with one fma, exact to fp32 rounding of the
-// (small) result for the dominant entries, and applies w = 2^-lo per row.
-__device__ inline void split_stat(double lse_nat, float& hi, float& w) {
+// (small) result for the dominant entries.
+__device__ inline void split_stat(double lse_nat, float& hi, float& lo) {
   const double l2 = lse_nat * kLog2eD;
   hi = (float)l2;
-  w = exp2f(-(float)(l2 - (double)hi));
+  lo = (float)(l2 - (double)hi);
 }
 
 // Row-major bf16 LDS tile with 16-byte chunks XOR-swizzled by f(row).  f is
@@ -227,6 +233,35 @@ __device__ inline void lse_block(const f32x16& St, const f32x16& Ss, float c, in
   ms = mns;
 }
 
+// Fixed-shift block sum: sum_r exp2(z_r * c - ref) over one 32x32 block
+// (masked entries contribute 0).
+template <bool MASK>
+__device__ inline void lse_block_fixed(const f32x16& St, const f32x16& Ss, float c, float rt, float rs,
+                                       int sw_base, int i, int n, int causal, int h, double& lt, double& ls) {
+  float at = 0.f, as = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float et = __builtin_amdgcn_exp2f(fmaf(St[r], c, -rt));
+    float es = __builtin_amdgcn_exp2f(fmaf(Ss[r], c, -rs));
+    if (MASK) {
+      const int j = sw_base + swept_of(r, h);
+      const bool ok = (!causal || j <= i) && j < n;
+      et = ok ? et : 0.f;
+      es = ok ? es : 0.f;
+    }
+    at += et;
+    as += es;
+  }
+  lt += (double)at;
+  ls += (double)as;
+}
+
+// Phase 1.  Every row's sum is taken against a fixed shift, the row's own
+// diagonal logit c*|x_i|^2 (the diagonal is always a kept entry), so the
+// inner loop needs no running maximum.  A term can only overflow if
+// <x_i, x_j> exceeds |x_i|^2 by more than ~88/scale; if any row of the
+// workgroup overflows, the workgroup redoes its rows with the online
+// maximum.  The stored statistic is exact either way.
 template <int D>
 __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, int nblk) {
   constexpr int KS = D / 16, RB = 2 * D, TB = Tile<D>::BYTES;
@@ -251,9 +286,22 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, 
   const int last = a.causal ? min(own0 + kOwn, n) - 1 : n - 1;
   const int ntiles = last / kSW + 1;
   const float c = a.scale * kLog2e;
-  float mt = -INFINITY, ms = -INFINITY;
-  double lsum_t = 0.0, lsum_s = 0.0;
 
+  // Shift: c * |x_i|^2 from the row's own fragments (each lane half holds half of d).
+  float nt = 0.f, ns = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float vt = (float)Bt[ks][e], vs = (float)Bs[ks][e];
+      nt = fmaf(vt, vt, nt);
+      ns = fmaf(vs, vs, ns);
+    }
+  nt += __shfl_xor(nt, 32);
+  ns += __shfl_xor(ns, 32);
+  const float ref_t = nt * c, ref_s = ns * c;
+
+  double lsum_t = 0.0, lsum_s = 0.0;
   Tile<D>::load(lds[0][0], xt, 0, n, wave, lane);
   Tile<D>::load(lds[0][1], xs, 0, n, wave, lane);
   for (int tI = 0; tI < ntiles; ++tI) {
@@ -271,12 +319,42 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, 
       f32x16 St, Ss;
       logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
       if (need_mask)
-        lse_block<true>(St, Ss, c, sw0 + 32 * sb, i, n, a.causal, h, mt, lsum_t, ms, lsum_s);
+        lse_block_fixed<true>(St, Ss, c, ref_t, ref_s, sw0 + 32 * sb, i, n, a.causal, h, lsum_t, lsum_s);
       else
-        lse_block<false>(St, Ss, c, sw0 + 32 * sb, i, n, a.causal, h, mt, lsum_t, ms, lsum_s);
+        lse_block_fixed<false>(St, Ss, c, ref_t, ref_s, sw0 + 32 * sb, i, n, a.causal, h, lsum_t, lsum_s);
     }
   }
-  // Combine the two lane halves that share owned row i.
+  lsum_t += __shfl_xor(lsum_t, 32);
+  lsum_s += __shfl_xor(lsum_s, 32);
+  const bool bad = i < n && !(lsum_t > 0.0 && lsum_t < 1e300 && lsum_s > 0.0 && lsum_s < 1e300);
+  if (!__syncthreads_or(bad)) {
+    // LSE = ln2 * (ref + log2 L), in fp64.
+    if (h == 0 && i < n) {
+      static_cast<double*>(a.lse_t)[bh * n + i] = ((double)ref_t + log2(lsum_t)) * kLn2D;
+      static_cast<double*>(a.lse_s)[bh * n + i] = ((double)ref_s + log2(lsum_s)) * kLn2D;
+    }
+    return;
+  }
+
+  // Fallback: online maximum.
+  float mt = -INFINITY, ms = -INFINITY;
+  lsum_t = 0.0;
+  lsum_s = 0.0;
+  for (int tI = 0; tI < ntiles; ++tI) {
+    const int buf = tI & 1, sw0 = tI * kSW;
+    __syncthreads();
+    Tile<D>::load(lds[buf][0], xt, sw0, n, wave, lane);
+    Tile<D>::load(lds[buf][1], xs, sw0, n, wave, lane);
+    wait_loads();
+    __syncthreads();
+    if (a.causal && sw0 > wown0 + 31) continue;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x16 St, Ss;
+      logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
+      lse_block<true>(St, Ss, c, sw0 + 32 * sb, i, n, a.causal, h, mt, lsum_t, ms, lsum_s);
+    }
+  }
   const float mt2 = __shfl_xor(mt, 32), ms2 = __shfl_xor(ms, 32);
   const double lt2 = __shfl_xor(lsum_t, 32), ls2 = __shfl_xor(lsum_s, 32);
   const float Mt = fmaxf(mt, mt2), Ms = fmaxf(ms, ms2);
@@ -285,9 +363,6 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, 
   // is evaluated in fp64 so the combination adds no fp32 rounding.
   const double Lt = lsum_t * exp2((double)fmaf(mt, c, -Mct)) + lt2 * exp2((double)fmaf(mt2, c, -Mct));
   const double Ls = lsum_s * exp2((double)fmaf(ms, c, -Mcs)) + ls2 * exp2((double)fmaf(ms2, c, -Mcs));
-  // LSE = ln2 * (M*c + log2 L), assembled in fp64 from the fp32 shift that
-  // the exponentials above actually used, so the stored statistic carries no
-  // rounding of M*c.
   if (h == 0 && i < n) {
     static_cast<double*>(a.lse_t)[bh * n + i] = ((double)Mct + log2(Lt)) * kLn2D;
     static_cast<double*>(a.lse_s)[bh * n + i] = ((double)Mcs + log2(Ls)) * kLn2D;
@@ -304,79 +379,73 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, 
 //   dX_s[i] ~ sum_{j!=i} dZ(i,j) x_j + sum_{j!=i} dZ(j,i) x_j
 //             - 2 (sum_{j!=i} dZ(i,j)) x_i.
 // Both sweeps skip the diagonal entry and the row sweep adds the last term
-// from its off-diagonal probability sums.  The probability of a dominant
+// from its running sum of off-diagonal dZ.  The probability of a dominant
 // diagonal is ~1 and its fp32 rounding (~6e-8) would otherwise swamp the
-// vanishing gradient of very peaky rows; the off-diagonal sums carry no
-// such cancellation.
+// vanishing gradient of very peaky rows.
 //
-// Probabilities: p = exp2(z*c - hi) and the true probability is p * w with
-// w = 2^-lo per row (split_stat).  The row sweep forms dZ/w_s(i) =
-// p_s - p_t * (w_t/w_s) and scales its accumulator by w_s(i) once; the column
-// sweep forms (p_s - p_t * w_t/w_s) * w_s per entry.  Identical teacher and
-// student inputs therefore give exactly zero.
+// Probabilities: with the fp64 statistic split as hi + lo (log2 units),
+// p = exp2(z*c - hi) is the true probability times 2^lo, |lo| <= one fp32
+// ulp of hi.  dZ uses p directly (the factor only moves off-diagonal
+// entries by ~1e-6 of themselves); the row KL applies it exactly:
+//   KL_i = ln2 * (2^-lo_t * sum_j p_t (a_t - a_s) + lo_s - lo_t),
+// using sum_j p_t 2^-lo_t = 1.  Identical teacher and student inputs give
+// exactly zero loss and gradient.
 // ---------------------------------------------------------------------------
 
 // Per-lane running state of a row sweep: per-block fp32 partials are added
 // into fp64 totals (rows of 32K keys add ~1000 blocks per lane).
 struct SweepState {
-  double kl = 0.0, off_t = 0.0, off_s = 0.0;
-  float pd_t = 0.f, pd_s = 0.f;
+  double kl = 0.0;          // sum_j p_t (a_t - a_s), log2 units
+  double dsum = 0.0;        // sum_{j != i} (p_s - p_t)
 };
 
 // Elementwise step on one 32x32 block, in place: St <- dZ * n.
 // SPECIAL: the block may hold masked or diagonal entries of this wave.
+// COL blocks read the swept rows' (hi_t, hi_s) from `stat`.
 template <int ROLE, bool SPECIAL>
 __device__ inline void block_elementwise(f32x16& St, const f32x16& Ss, float c, int sw_base, int o, int n,
-                                         int causal, int h, float l2t, float l2s, float wts,
-                                         const float4* stat, SweepState& S) {
-  float kl = 0.f, off_t = 0.f, off_s = 0.f;
+                                         int causal, int h, float l2t, float l2s, const float2* stat,
+                                         SweepState& S) {
+  float kl = 0.f, dsum = 0.f;
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * g4 + e;
-      float bt = l2t, bs = l2s, rr = wts, wsr = 1.f;
+      float bt = l2t, bs = l2s;
       if (ROLE == ROLE_COL) {
-        const float4 st = stat[8 * g4 + 4 * h + e];
+        const float2 st = stat[8 * g4 + 4 * h + e];
         bt = st.x;
         bs = st.y;
-        rr = st.z;
-        wsr = st.w;
       }
       float at = fmaf(St[r], c, -bt);
       float as = fmaf(Ss[r], c, -bs);
       float pt = __builtin_amdgcn_exp2f(at);
       float ps = __builtin_amdgcn_exp2f(as);
-      bool offdiag = true;
+      float dz;
       if (SPECIAL) {
         const int sw = sw_base + swept_of(r, h);
         const int ii = ROLE == ROLE_ROW ? o : sw;
         const int jj = ROLE == ROLE_ROW ? sw : o;
         const bool ok = (!causal || jj <= ii) && sw < n;
-        const bool diag = ok && sw == o;
         pt = ok ? pt : 0.f;
         ps = ok ? ps : 0.f;
         at = ok ? at : 0.f;
         as = ok ? as : 0.f;
-        if (ROLE == ROLE_ROW) {
-          S.pd_t = diag ? pt : S.pd_t;
-          S.pd_s = diag ? ps : S.pd_s;
-        }
-        offdiag = !diag;
+        dz = (ok && sw != o) ? ps - pt : 0.f;
+      } else {
+        dz = ps - pt;
       }
       if (ROLE == ROLE_ROW) {
         kl = fmaf(pt, at - as, kl);
-        off_t += offdiag ? pt : 0.f;
-        off_s += offdiag ? ps : 0.f;
+        dsum += dz;
       }
-      const float dz = ROLE == ROLE_ROW ? fmaf(-pt, rr, ps) : fmaf(-pt, rr, ps) * wsr;
-      St[r] = offdiag ? dz : 0.f;
+      St[r] = dz;
     }
   }
   if (ROLE == ROLE_ROW) {
     S.kl += (double)kl;
-    S.off_t += (double)off_t;
-    S.off_s += (double)off_s;
+    S.dsum += (double)dsum;
   }
 }
 
@@ -385,8 +454,8 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs 
   constexpr int KS = D / 16, DB = D / 32, RB = 2 * D, TB = Tile<D>::BYTES;
   constexpr int NSTAT = ROLE == ROLE_COL ? 2 : 1;
   __shared__ __attribute__((aligned(1024))) char lds[2][2][TB];
-  // COL: per swept row (hi_t, hi_s, w_t/w_s, w_s), double-buffered.
-  __shared__ float4 lstat[NSTAT][ROLE == ROLE_COL ? kSW : 1];
+  // COL: per swept row (hi_t, hi_s), double-buffered.
+  __shared__ float2 lstat[NSTAT][ROLE == ROLE_COL ? kSW : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
   const int64_t bid = blockIdx.x;
@@ -407,12 +476,10 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) { Bt[ks] = load_own(rt, ks, h); Bs[ks] = load_own(rs, ks, h); }
   }
-  float l2t = 0.f, l2s = 0.f, wts = 1.f, ws = 1.f;      // owned-row statistics (ROW)
+  float l2t = 0.f, l2s = 0.f, lot = 0.f, los = 0.f;     // owned-row statistics (ROW)
   if (ROLE == ROLE_ROW && o < n) {
-    float wt;
-    split_stat(glt[o], l2t, wt);
-    split_stat(gls[o], l2s, ws);
-    wts = wt / ws;
+    split_stat(glt[o], l2t, lot);
+    split_stat(gls[o], l2s, los);
   }
   int t_begin, t_end;
   if (ROLE == ROLE_ROW) {
@@ -437,12 +504,12 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs 
   };
   auto put_stat = [&](int b, int tile) {
     const int g = tile * kSW + tid;
-    float ht = 0.f, hs = 0.f, ft = 1.f, fs = 1.f;
+    float ht = 0.f, hs = 0.f, ft, fs;
     if (g < n) {
       split_stat(nlt, ht, ft);
       split_stat(nls, hs, fs);
     }
-    lstat[b][tid] = make_float4(ht, hs, ft / fs, fs);
+    lstat[b][tid] = make_float2(ht, hs);
   };
 
   Tile<D>::load(lds[0][0], xt, t_begin * kSW, n, wave, lane);
@@ -477,64 +544,102 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs 
     const bool special = need_mask || (sw0 <= wown0 + 31 && sw0 + kSW - 1 >= wown0);
     const char* lt = lds[buf][0];
     const char* ls = lds[buf][1];
-    const float4* stat0 = &lstat[ROLE == ROLE_COL ? buf : 0][0];
-    const float4* stat1 = &lstat[ROLE == ROLE_COL ? buf : 0][ROLE == ROLE_COL ? 32 : 0];
+    const float2* stat0 = &lstat[ROLE == ROLE_COL ? buf : 0][0];
+    const float2* stat1 = &lstat[ROLE == ROLE_COL ? buf : 0][ROLE == ROLE_COL ? 32 : 0];
     if (LMR_SWEEP_PIPE && !special) {
-      // Software pipeline over the two sub-blocks: the logit MFMAs of
-      // sub-block 1 run under the elementwise work of sub-block 0, and the
-      // contraction MFMAs of sub-block 0 under the elementwise work of 1.
-      f32x16 St0, Ss0, St1, Ss1;
-      logits<D>(lt, ls, Bt, Bs, St0, Ss0, 0, lane);
-      logits<D>(lt, ls, Bt, Bs, St1, Ss1, 1, lane);
-      block_elementwise<ROLE, false>(St0, Ss0, c, sw0, o, n, a.causal, h, l2t, l2s, wts, stat0, S);
+      // Software pipeline over the two sub-blocks in fenced stages.  Every
+      // stage first issues all of its LDS fragment reads, then interleaves
+      // its MFMAs with independent elementwise work:
+      //   0: logits(0)    1: logits(1) | elementwise(0)
+      //   2: contract(0) | elementwise(1)    3: contract(1)
+      constexpr int KS2 = KS;
+      bf16x8 At[KS2], As[KS2];
+      f32x16 St0 = {}, Ss0 = {}, St1 = {}, Ss1 = {};
+      const int rr0 = lane & 31;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) { At[ks] = Tile<D>::frag(lt, rr0, ks, h); As[ks] = Tile<D>::frag(ls, rr0, ks, h); }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) { St0 = mma(At[ks], Bt[ks], St0); Ss0 = mma(As[ks], Bs[ks], Ss0); }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) { At[ks] = Tile<D>::frag(lt, 32 + rr0, ks, h); As[ks] = Tile<D>::frag(ls, 32 + rr0, ks, h); }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) { St1 = mma(At[ks], Bt[ks], St1); Ss1 = mma(As[ks], Bs[ks], Ss1); }
+      block_elementwise<ROLE, false>(St0, Ss0, c, sw0, o, n, a.causal, h, l2t, l2s, stat0, S);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);      // all fragment reads
 #pragma unroll
       for (int k = 0; k < 2 * KS; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // then VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, LMR_PIPE_V1, 0); // then VALU
       }
-      if constexpr (WITH_DX) contract<D>(St0, ls, 0, lane, acc);
-      block_elementwise<ROLE, false>(St1, Ss1, c, sw0 + 32, o, n, a.causal, h, l2t, l2s, wts, stat1, S);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (WITH_DX) {
+        bf16x8 Ar[2][DB];
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) Ar[q2][db] = Tile<D>::tr_frag(ls, q2, db, lane);
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = St0[8 * q2 + e];
+          const bf16x8 bdz = pack8(v);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = mma(Ar[q2][db], bdz, acc[db]);
+        }
+        block_elementwise<ROLE, false>(St1, Ss1, c, sw0 + 32, o, n, a.causal, h, l2t, l2s, stat1, S);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 0);     // transpose reads (2 per fragment)
 #pragma unroll
         for (int k = 0; k < 2 * DB; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, LMR_PIPE_V2, 0);
         }
-        contract<D>(St1, ls, 1, lane, acc);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) Ar[q2][db] = Tile<D>::tr_frag(ls, 2 + q2, db, lane);
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = St1[8 * q2 + e];
+          const bf16x8 bdz = pack8(v);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = mma(Ar[q2][db], bdz, acc[db]);
+        }
+      } else {
+        block_elementwise<ROLE, false>(St1, Ss1, c, sw0 + 32, o, n, a.causal, h, l2t, l2s, stat1, S);
       }
     } else {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         f32x16 St, Ss;
         logits<D>(lt, ls, Bt, Bs, St, Ss, sb, lane);
-        const float4* stat = sb ? stat1 : stat0;
+        const float2* stat = sb ? stat1 : stat0;
         if (special)
-          block_elementwise<ROLE, true>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, wts, stat, S);
+          block_elementwise<ROLE, true>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
         else
-          block_elementwise<ROLE, false>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, wts, stat, S);
+          block_elementwise<ROLE, false>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
         if constexpr (WITH_DX) contract<D>(St, ls, sb, lane, acc);
       }
     }
   }
 
-  float corr = 0.f;                                      // ROW: -2 * sum_{j!=i} dZ(i,j) / w_s(i) * n
+  float corr = 0.f;                                      // ROW: -2 * sum_{j!=i} dZ(i,j) * n
   if (ROLE == ROLE_ROW) {
     S.kl += __shfl_xor(S.kl, 32);
-    S.off_t += __shfl_xor(S.off_t, 32);
-    S.off_s += __shfl_xor(S.off_s, 32);
-    S.pd_t += __shfl_xor(S.pd_t, 32);
-    S.pd_s += __shfl_xor(S.pd_s, 32);
-    const double sum_t = S.off_t + (double)S.pd_t, sum_s = S.off_s + (double)S.pd_s;
-    // KL = sum_j r_t (log2 r_t - log2 r_s) ln2 with r = p / sum p.
-    const double klr = S.kl / sum_t - log2(sum_t) + log2(sum_s);
+    S.dsum += __shfl_xor(S.dsum, 32);
+    const double klr = exp2(-(double)lot) * S.kl + (double)los - (double)lot;
     if (h == 0 && o < n && a.row_kl != nullptr) a.row_kl[bh * n + o] = (float)(klr * kLn2D);
-    corr = (float)(-2.0 * (S.off_s - S.off_t * (double)wts));
+    corr = (float)(-2.0 * S.dsum);
   }
   if constexpr (WITH_DX) {
     if (o < n) {
       float* dst = a.dx + (bh * (int64_t)n + o) * D;
       const uint16_t* xo = reinterpret_cast<const uint16_t*>(xs + (int64_t)o * RB);
-      const float gs = ROLE == ROLE_ROW ? a.grad_scale * ws : a.grad_scale;
+      const float gs = a.grad_scale;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll

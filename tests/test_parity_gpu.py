@@ -181,3 +181,21 @@ def test_split_mode_is_bitwise_deterministic(gpu_lib):
         outs.append((float(loss.cpu()), dx.cpu().numpy()))
     for o in outs[1:]:
         assert o[0] == outs[0][0] and np.array_equal(o[1], outs[0][1])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_overflowing_shift_takes_the_exact_fallback(gpu_lib, causal):
+    # Row 3 has a huge norm, so for the rows after it a logit exceeds the
+    # row's own diagonal logit by far more than fp32 exp2 can represent;
+    # phase 1 must fall back to the online maximum and stay exact.
+    n, d = 150, 64
+    rng = np.random.default_rng(12)
+    xt = rng.standard_normal((1, 2, n, d))
+    xt[:, :, 3] *= 30.0
+    xs = xt + 0.3 * rng.standard_normal((1, 2, n, d))
+    xt, xs = si.round_bf16_bits(xt), si.round_bf16_bits(xs)
+    got = _run(gpu_lib, xt, xs, "bf16", 0.125, causal=causal)
+    a, b = widen(xt, "bf16"), widen(xs, "bf16")
+    ref = oracle.relation_kl(a, b, 0.125, causal)
+    assert np.all(np.isfinite(got["lse_t"])) and np.all(np.isfinite(got["dx"]))
+    _compare(got, ref, "bf16", n, _logit_bound(a, b, 0.125))
