@@ -38,6 +38,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-n", type=int, default=0,
                    help="sequence length of the oracle sample (default: the workload's n)")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="before warm-up, run one fp32 elementwise copy (y = x * 1) of this many MiB; "
+                        "its FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
+    p.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "COPY_MIB"),
+                   help="write the markdown summary of rocprofv3 kernel-trace/stats and FETCH_SIZE/WRITE_SIZE "
+                        "runs of this script to stdout and exit")
+    p.add_argument("--trace-cmd", default="", help="(with --summarize) command lines to record in the summary")
     return p.parse_args()
 
 
@@ -46,30 +53,159 @@ def causal_pairs(n: int) -> int:
 
 
 def cpu_baseline(w, maps, sample_n: int):
-    """Time the fp64 oracle on one head-map (Q/Q, b=0, h=0) on the host cores."""
+    """Time the fp64 oracle on two head-maps (Q/Q and K/K of b=0, h=0) on the host cores."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count() or 1])
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
-    m = maps["Q"]
-    xt, xs = m.head64(0, 0)
     n = sample_n or w.n
-    xt, xs = xt[:n], xs[:n]
-    t0 = time.perf_counter()
-    r = oracle.relation_kl_head(xt, xs, w.scale, True)
-    dt = time.perf_counter() - t0
-    flops = 12.0 * w.d * causal_pairs(n)
-    assert np.isfinite(r["loss"])
+    names = [k for k in ("Q", "K") if k in maps] or list(maps)[:1]
+    dt = 0.0
+    for name in names:
+        xt, xs = maps[name].head64(0, 0)
+        xt, xs = xt[:n], xs[:n]
+        t0 = time.perf_counter()
+        r = oracle.relation_kl_head(xt, xs, w.scale, True)
+        dt += time.perf_counter() - t0
+        assert np.isfinite(r["loss"])
+        del r
+    flops = len(names) * 12.0 * w.d * causal_pairs(n)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": dt,
-            "sample": f"one head-map (Q/Q, b=0, h=0) of {w.name} at n={n}, d={w.d}: dense fp64 "
-                      f"numpy oracle (loss, LSE, row KL, dX_s); algorithmic flops 12*d*n(n+1)/2"}
+            "seconds": round(dt, 3),
+            "sample": f"{len(names)} head-maps ({', '.join(k + '/' + k for k in names)} of b=0, h=0) of {w.name} "
+                      f"at n={n}, d={w.d}: dense fp64 numpy oracle (loss, LSE, row KL, dX_s); "
+                      f"algorithmic flops 12*d*n(n+1)/2 per head-map"}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (kernel trace + HBM traffic), kept as text under profiles/
+# ---------------------------------------------------------------------------
+def library_source_id() -> str:
+    """Stamp of the built library (hash of its sources); loading it needs no GPU."""
+    import linear_memory_relation_amd as lmr
+    from linear_memory_relation_amd.build import source_id
+    got = lmr.source_id()
+    if got != source_id():
+        raise SystemExit(f"liblarard.so (src {got}) was not built from the current sources "
+                         f"(src {source_id()}); rebuild before profiling or summarising")
+    return got
+
+
+def kernel_kind(name: str) -> str:
+    if "lse_fwd_kernel" in name:
+        return "lse_fwd"
+    if "kl_sweep_kernel" in name:
+        return "kl_rows" if ", 0, " in name else "kl_cols"
+    if "reduce_rows_kernel" in name or "reduce_final_kernel" in name:
+        return "reduce"
+    if "MulFunctor" in name:
+        return "copy_calibration"
+    return "other"
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return rows
+
+
+def _pmc_per_dispatch(d: str, counter: str):
+    """Mean of `counter` (KiB) per dispatch, by kernel name."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id")))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {k: (float(np.mean(v)), len(v)) for k, v in out.items()}
+
+
+def summarize(trace_dir: str, fetch_dir: str, write_dir: str, copy_mib: str, cmds: str) -> str:
+    copy_bytes = int(copy_mib) * 2 ** 20
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    lines = ["# Kernel time and HBM traffic of one relation-KL step (llama2_16k workload)", ""]
+    lines += ["Workload: B=1, H=32, n=16384, d=128, bf16, maps Q/Q, K/K, V/V, causal, split dX mode.", ""]
+    lines += [f"Library: {__import__('linear_memory_relation_amd').version()}", ""]
+    lines += ["Commands (run from the repository root; rocprofv3 wrote CSV under the -d directory):", "", "```"]
+    lines += [c for c in cmds.split(";;") if c] + ["```", ""]
+    lines += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", ""]
+    lines += ["| kernel | kind | calls | avg ms | min ms | max ms | share of GPU time |", "|---|---|---|---|---|---|---|"]
+    def col(r, *names):
+        for k in names:
+            for kk in r:
+                if kk.lower().replace("_", "") == k.lower().replace("_", ""):
+                    return r[kk]
+        raise SystemExit(f"column {names} not in {list(r)}")
+    for r in sorted(stats, key=lambda r: -float(col(r, "TotalDurationNs"))):
+        name = col(r, "Name", "KernelName", "Kernel_Name")
+        lines.append(f"| `{name[:90]}` | {kernel_kind(name)} | {col(r, 'Calls')} | "
+                     f"{float(col(r, 'AverageNs')) / 1e6:.4f} | {float(col(r, 'MinNs')) / 1e6:.4f} | "
+                     f"{float(col(r, 'MaxNs')) / 1e6:.4f} | {float(col(r, 'Percentage')):.2f}% |")
+    cal = [k for k in fetch if kernel_kind(k) == "copy_calibration"]
+    if not cal or not [k for k in write if kernel_kind(k) == "copy_calibration"]:
+        raise SystemExit("calibration copy kernel not found in the counter runs")
+    f_cal = fetch[cal[0]][0] * 1024 / copy_bytes
+    w_cal = write[[k for k in write if kernel_kind(k) == "copy_calibration"][0]][0] * 1024 / copy_bytes
+    lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", ""]
+    lines += [f"Calibration: an fp32 copy of {copy_mib} MiB reads and writes {copy_bytes} bytes; its counters read "
+              f"FETCH_SIZE x {f_cal:.4f} and WRITE_SIZE x {w_cal:.4f} of that, and every figure below is divided "
+              f"by these factors.", ""]
+    lines += ["| kernel | kind | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (calibrated) |",
+              "|---|---|---|---|---|---|"]
+    traffic = {}
+    for name, (fk, cnt) in sorted(fetch.items(), key=lambda kv: -kv[1][0]):
+        wk = write.get(name, (0.0, 0))[0]
+        tb = fk * 1024 / f_cal + wk * 1024 / w_cal
+        kind = kernel_kind(name)
+        if kind in ("lse_fwd", "kl_rows", "kl_cols"):
+            traffic[kind] = tb
+        lines.append(f"| `{name[:90]}` | {kind} | {cnt} | {fk:.1f} | {wk:.1f} | {tb:.4e} |")
+    lines += ["", "Machine-readable (read by bench.py while the kernel sources are unchanged):", ""]
+    lines.append(f"library_source_id: {library_source_id()}")
+    for k, v in sorted(traffic.items()):
+        lines.append(f"traffic_bytes_per_launch {k}: {v:.6e}")
+    return "\n".join(lines) + "\n"
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kernel_trace_and_traffic_llama2_16k.md")
+
+
+def recorded_traffic(kind: str, workload: str):
+    """Calibrated HBM bytes per launch of `kind` from the committed summary, or None when the
+    summary is missing, covers another workload or was taken on a library built from other sources."""
+    import linear_memory_relation_amd as lmr
+    if workload != "llama2_16k" or not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    src, val = None, None
+    with open(TRAFFIC_SUMMARY) as f:
+        for line in f:
+            if line.startswith("library_source_id:"):
+                src = line.split(":", 1)[1].strip()
+            if line.startswith(f"traffic_bytes_per_launch {kind}:"):
+                val = float(line.split(":", 1)[1])
+    if src != lmr.source_id():
+        return None
+    return val
 
 
 def main():
     args = parse()
+    if args.summarize:
+        sys.stdout.write(summarize(*args.summarize, args.trace_cmd))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this kernel shards by heads "
               f"with no exchange but a scalar loss sum, and multi-GPU runs are not part of this build.",
@@ -109,6 +245,12 @@ def main():
     dx_bytes = sum(b["dx"].numel() * 4 for b in bufs)
     stat_bytes = sum(b["lse_t"].numel() * (8 + 8 + 4) + b["partials"].numel() * 8 for b in bufs)
     torch.cuda.synchronize()
+    if args.calib_copy_mib > 0:
+        src = torch.ones(args.calib_copy_mib * 2 ** 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.reset_peak_memory_stats()
 
     kinds = ["lse_fwd", "kl_rows", "kl_cols", "reduce"]
@@ -192,6 +334,7 @@ def main():
     dom = max(kinds, key=lambda k: kern[k]["share"])
     dom_flops = float(np.mean([alg[dom] * units(b) for b in bufs]))
     achieved = dom_flops / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+    traffic = recorded_traffic(dom, w.name)
     value = step_flops / (ms_step * 1e-3) / 1e12
 
     out = {
@@ -212,8 +355,9 @@ def main():
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
-                     "alg_flops_per_launch": dom_flops},
+                     "traffic": traffic,
+                     "alg_flops_per_launch": dom_flops,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"},
         "kernels": kern,
         "ms_per_step_one_call": round(ms_step_oneshot, 4),
         "wall_s_timed": round(wall, 3),

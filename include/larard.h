@@ -150,7 +150,8 @@ const char* larard_status_str(larard_status status);
 /* Text of the last LARARD_E_HIP / validation failure on this thread ("" if none). */
 const char* larard_last_error(void);
 
-/* Library version string, e.g. "larard 0.1.0 gfx950". */
+/* Library version string, e.g. "larard 0.1.0 gfx950 (src 0123456789abcdef)";
+ * the src field is a hash of the sources the library was built from. */
 const char* larard_version(void);
 
 #ifdef __cplusplus

@@ -205,3 +205,9 @@ def loss(xt: torch.Tensor, xs: torch.Tensor, scale: Optional[float] = None, caus
 
 def version() -> str:
     return load().larard_version().decode()
+
+
+def source_id() -> str:
+    """Hash of the sources the loaded library was built from (from its version string)."""
+    v = version()
+    return v.split("(src ", 1)[1].rstrip(")") if "(src " in v else ""

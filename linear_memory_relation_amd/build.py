@@ -20,6 +20,8 @@ LIB = os.path.join(PKG, "liblarard.so")
 ARCH = "gfx950"
 
 SOURCES = ["kernels.hip", "wide.hip", "api.cpp"]
+# Everything the library is built from; its hash is stamped into larard_version().
+STAMPED = [os.path.join(CSRC, f) for f in (*SOURCES, "launch.h")] + [os.path.join(INCLUDE, "larard.h")]
 
 # Packed fp32 VALU forms are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -34,10 +36,20 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library cannot be built")
 
 
-def _compile(src: str, verbose: bool) -> str:
+def source_id() -> str:
+    """First 16 hex digits of the SHA-256 of the library's sources (the stamp in larard_version())."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in STAMPED:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _compile(src: str, verbose: bool, stamp: str) -> str:
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, f'-DLARARD_SOURCE_ID="{stamp}"', "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,8 +64,9 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile every source and link liblarard.so; returns the library path."""
+    stamp = source_id()
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, verbose, stamp), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:

@@ -263,6 +263,9 @@ const char* larard_status_str(larard_status status) {
 
 const char* larard_last_error(void) { return g_last_error.c_str(); }
 
-const char* larard_version(void) { return "larard 0.1.0 gfx950"; }
+#ifndef LARARD_SOURCE_ID
+#define LARARD_SOURCE_ID "unstamped"
+#endif
+const char* larard_version(void) { return "larard 0.1.0 gfx950 (src " LARARD_SOURCE_ID ")"; }
 
 }  // extern "C"

@@ -34,6 +34,9 @@ def test_every_declared_symbol_is_exported(lib):
 def test_version_and_status_strings(lib):
     import linear_memory_relation_amd as lmr
     assert "gfx950" in lmr.version()
+    # the loaded library was built from the sources in this tree
+    from linear_memory_relation_amd.build import source_id
+    assert lmr.source_id() == source_id()
     for code in range(5):
         assert lib.larard_status_str(code).decode().startswith("LARARD_")
 
