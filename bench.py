@@ -313,6 +313,24 @@ def main():
     ms_step_oneshot = s2.elapsed_time(e2) / args.steps
     losses = {b["name"]: float(b["loss"].cpu()) for b in bufs}
 
+    # Forward-only loss (one phase-1 sweep with the KL accumulator + reduce),
+    # timed the same way: 2 GEMM-units per head-map.
+    def fwd_step():
+        for b in bufs:
+            lmr.kl_fwd(b["xt"], b["xs"], scale, True, b["lse_t"], b["lse_s"], b["row_kl"])
+            lmr.reduce_loss(b["row_kl"], b["partials"], b["loss"], 1.0)
+    for _ in range(args.warmup):
+        fwd_step()
+    torch.cuda.synchronize()
+    s3, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s3.record()
+    for _ in range(args.steps):
+        fwd_step()
+    e3.record()
+    torch.cuda.synchronize()
+    ms_fwd = s3.elapsed_time(e3) / args.steps
+    losses_fwd = {b["name"]: float(b["loss"].cpu()) for b in bufs}
+
     # Algorithmic work.  Per head-map P = n(n+1)/2 unmasked pairs, one
     # contraction = 2*d*P flops.  Phase 1: 2 contractions; the row sweep
     # carries phase 2's recompute (2) and the row term (1); the column sweep's
@@ -366,6 +384,12 @@ def main():
                    "bhn_bound_bytes": int(sum(20 * b["B"] * b["H"] * b["n"] for b in bufs)),
                    "dense_fp32_map_bytes_one_matrix": int(sum(4 * b["B"] * b["H"] * b["n"] ** 2 for b in bufs))},
         "losses": losses,
+        "forward_only": {"ms_per_step": round(ms_fwd, 4),
+                         "tflops": round(sum(2 * units(b) for b in bufs) / (ms_fwd * 1e-3) / 1e12, 3),
+                         "pct_bf16_peak": round(100 * sum(2 * units(b) for b in bufs) / (ms_fwd * 1e-3) / 1e12
+                                                / PEAK_BF16_TFLOPS, 2),
+                         "losses": losses_fwd,
+                         "what": "larard_kl_fwd + reduce per map; algorithmic flops 2 GEMM-units per head-map"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, maps, args.cpu_sample_n)

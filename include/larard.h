@@ -84,6 +84,19 @@ larard_status larard_lse_fwd(const void* x_t, const void* x_s, larard_dtype dtyp
                              float scale, int causal,
                              void* lse_t, void* lse_s, void* stream);
 
+/* Forward-only loss in one sweep (notes page, "Key designs" items 1 and 3;
+ * the KL needs only the logits and both row statistics): phase 1 extended
+ * with a teacher-weighted log-ratio accumulator.  Writes lse_t and lse_s as
+ * larard_lse_fwd does (fp64 [B,H,n], natural log) and
+ *   row_kl[b,h,i] = KL(R_t(i,:) || R_s(i,:))          (fp32, not scaled)
+ * at the cost of phase 1 alone (2 of the 6 contractions of the full path).
+ * All three outputs are required.  The row KL agrees with larard_kl_bwd's to
+ * fp32 rounding, not bit for bit. */
+larard_status larard_kl_fwd(const void* x_t, const void* x_s, larard_dtype dtype,
+                            int64_t B, int64_t H, int64_t n, int64_t d,
+                            float scale, int causal,
+                            void* lse_t, void* lse_s, float* row_kl, void* stream);
+
 /* Phase 2 (notes page, "Key designs" item 3): recomputes the logit tiles,
  * rebuilds R_t and R_s from lse_t / lse_s (which must come from
  * larard_lse_fwd with the same inputs and arguments), and writes
@@ -128,7 +141,8 @@ larard_status larard_reduce_loss(const float* row_kl, int64_t B, int64_t H, int6
 /* Whole path for one relation map: phase 1, phase 2 and a deterministic
  * fp64 reduction.  Writes
  *   *loss = loss_scale * sum_{b,h} (1/n) sum_i KL_i        (device fp32 scalar)
- * and dx_s as in larard_kl_bwd (NULL = loss only).  The workspace (device,
+ * and dx_s as in larard_kl_bwd.  dx_s == NULL computes the loss only, with
+ * larard_kl_fwd's single sweep instead of phase 1 + phase 2.  The workspace (device,
  * 256-byte aligned, >= larard_workspace_bytes(dtype,B,H,n)) holds LSE_t, LSE_s,
  * row_kl and partial sums; after return-and-sync it contains them in that
  * order (see larard_workspace_layout).  n == 0 writes *loss = 0. */

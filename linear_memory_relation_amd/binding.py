@@ -46,6 +46,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.larard_workspace_layout.restype = i32
     lib.larard_lse_fwd.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, vp]
     lib.larard_lse_fwd.restype = i32
+    lib.larard_kl_fwd.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, vp, vp]
+    lib.larard_kl_fwd.restype = i32
     lib.larard_kl_bwd.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, f32, vp, vp, i32, vp]
     lib.larard_kl_bwd.restype = i32
     lib.larard_kl_bwd_rows.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, f32, vp, vp, vp]
@@ -131,6 +133,24 @@ def lse_fwd(xt: torch.Tensor, xs: torch.Tensor, scale: Optional[float] = None, c
                                _ptr(lse_t), _ptr(lse_s), _stream())
     _check(st, "larard_lse_fwd")
     return lse_t, lse_s
+
+
+def kl_fwd(xt: torch.Tensor, xs: torch.Tensor, scale: Optional[float] = None, causal: bool = True,
+           lse_t: Optional[torch.Tensor] = None, lse_s: Optional[torch.Tensor] = None,
+           row_kl: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Forward-only sweep: (lse_t, lse_s, row_kl) -- fp64, fp64, fp32 [B, H, n] -- in one pass."""
+    B, H, n, d = _shape(xt, xs)
+    scale = default_scale(d) if scale is None else float(scale)
+    if lse_t is None:
+        lse_t = torch.empty((B, H, n), dtype=stat_dtype(xt), device=xt.device)
+    if lse_s is None:
+        lse_s = torch.empty((B, H, n), dtype=stat_dtype(xt), device=xt.device)
+    if row_kl is None:
+        row_kl = torch.empty((B, H, n), dtype=torch.float32, device=xt.device)
+    st = load().larard_kl_fwd(_ptr(xt), _ptr(xs), _dtype_code(xt), B, H, n, d, scale, int(causal),
+                              _ptr(lse_t), _ptr(lse_s), _ptr(row_kl), _stream())
+    _check(st, "larard_kl_fwd")
+    return lse_t, lse_s, row_kl
 
 
 def kl_bwd(xt: torch.Tensor, xs: torch.Tensor, lse_t: torch.Tensor, lse_s: torch.Tensor,

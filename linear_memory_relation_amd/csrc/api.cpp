@@ -153,6 +153,24 @@ larard_status larard_lse_fwd(const void* x_t, const void* x_s, larard_dtype dtyp
   return LARARD_OK;
 }
 
+larard_status larard_kl_fwd(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
+                            int64_t n, int64_t d, float scale, int causal, void* lse_t, void* lse_s,
+                            float* row_kl, void* stream) {
+  larard_status s = check_common(x_t, x_s, dtype, B, H, n, d, scale);
+  if (s != LARARD_OK) return s;
+  if (n == 0) return LARARD_OK;
+  if (lse_t == nullptr || lse_s == nullptr) return fail(LARARD_E_INVALID, "lse_t / lse_s must not be NULL");
+  if (!aligned(lse_t, stat_bytes(dtype)) || !aligned(lse_s, stat_bytes(dtype)))
+    return fail(LARARD_E_INVALID, "lse buffers must be aligned to their element size");
+  if (row_kl == nullptr || !aligned(row_kl, 4)) return fail(LARARD_E_INVALID, "row_kl must be a 4-byte aligned pointer");
+  lmr::SweepArgs a = make_args(x_t, x_s, dtype, B, H, n, d, scale, causal);
+  a.lse_t = lse_t;
+  a.lse_s = lse_s;
+  a.row_kl = row_kl;
+  const hipError_t e = lmr::launch_kl_fwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LARARD_OK : hip_fail(e, "kl_fwd launch");
+}
+
 larard_status larard_kl_bwd(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
                             int64_t n, int64_t d, float scale, int causal, const void* lse_t,
                             const void* lse_s, float loss_scale, float* row_kl, float* dx_s, int dx_mode,
@@ -198,11 +216,18 @@ larard_status larard_loss(const void* x_t, const void* x_s, larard_dtype dtype, 
   lmr::SweepArgs a = make_args(x_t, x_s, dtype, B, H, n, d, scale, causal);
   a.lse_t = lse_t;
   a.lse_s = lse_s;
-  hipError_t e = lmr::launch_lse_fwd(a, st);
-  if (e != hipSuccess) return hip_fail(e, "lse_fwd launch");
   a.row_kl = row_kl;
-  a.dx = dx_s;
-  if ((s = run_kl_bwd(a, loss_scale, st)) != LARARD_OK) return s;
+  hipError_t e;
+  if (dx_s == nullptr) {
+    // Loss only: LSE and row KL in one phase-1 sweep.
+    e = lmr::launch_kl_fwd(a, st);
+    if (e != hipSuccess) return hip_fail(e, "kl_fwd launch");
+  } else {
+    e = lmr::launch_lse_fwd(a, st);
+    if (e != hipSuccess) return hip_fail(e, "lse_fwd launch");
+    a.dx = dx_s;
+    if ((s = run_kl_bwd(a, loss_scale, st)) != LARARD_OK) return s;
+  }
   e = lmr::launch_reduce(row_kl, a.bh, a.n, loss_scale, partials, loss, st);
   if (e != hipSuccess) return hip_fail(e, "loss reduction launch");
   return LARARD_OK;

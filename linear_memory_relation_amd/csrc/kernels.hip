@@ -234,15 +234,18 @@ __device__ inline void lse_block(const f32x16& St, const f32x16& Ss, float c, in
 }
 
 // Fixed-shift block sum: sum_r exp2(z_r * c - ref) over one 32x32 block
-// (masked entries contribute 0).
-template <bool MASK>
+// (masked entries contribute 0).  KL: also w += sum_r exp2(a_t)(a_t - a_s)
+// with a_m = z_m * c - ref_m, the teacher-weighted log-ratio numerator.
+template <bool MASK, bool KL>
 __device__ inline void lse_block_fixed(const f32x16& St, const f32x16& Ss, float c, float rt, float rs,
-                                       int sw_base, int i, int n, int causal, int h, double& lt, double& ls) {
-  float at = 0.f, as = 0.f;
+                                       int sw_base, int i, int n, int causal, int h, double& lt, double& ls,
+                                       double& w) {
+  float at = 0.f, as = 0.f, aw = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    float et = __builtin_amdgcn_exp2f(fmaf(St[r], c, -rt));
-    float es = __builtin_amdgcn_exp2f(fmaf(Ss[r], c, -rs));
+    const float xt = fmaf(St[r], c, -rt), xs = fmaf(Ss[r], c, -rs);
+    float et = __builtin_amdgcn_exp2f(xt);
+    float es = __builtin_amdgcn_exp2f(xs);
     if (MASK) {
       const int j = sw_base + swept_of(r, h);
       const bool ok = (!causal || j <= i) && j < n;
@@ -251,9 +254,27 @@ __device__ inline void lse_block_fixed(const f32x16& St, const f32x16& Ss, float
     }
     at += et;
     as += es;
+    if (KL) aw = fmaf(et, xt - xs, aw);
   }
   lt += (double)at;
   ls += (double)as;
+  if (KL) w += (double)aw;
+}
+
+// Teacher-weighted log-ratio against fixed statistics hi_t, hi_s (log2
+// units): k += sum_r exp2(a_t) (a_t - a_s), a_m = z_m * c - hi_m.
+__device__ inline void kl_block_stat(const f32x16& St, const f32x16& Ss, float c, float ht, float hs,
+                                     int sw_base, int i, int n, int causal, int h, double& k) {
+  float acc = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = sw_base + swept_of(r, h);
+    const bool ok = (!causal || j <= i) && j < n;
+    const float xt = fmaf(St[r], c, -ht), xs = fmaf(Ss[r], c, -hs);
+    const float pt = ok ? __builtin_amdgcn_exp2f(xt) : 0.f;
+    acc = fmaf(pt, ok ? xt - xs : 0.f, acc);
+  }
+  k += (double)acc;
 }
 
 // Phase 1.  Every row's sum is taken against a fixed shift, the row's own
@@ -262,7 +283,15 @@ __device__ inline void lse_block_fixed(const f32x16& St, const f32x16& Ss, float
 // <x_i, x_j> exceeds |x_i|^2 by more than ~88/scale; if any row of the
 // workgroup overflows, the workgroup redoes its rows with the online
 // maximum.  The stored statistic is exact either way.
-template <int D>
+//
+// KL (forward-only loss): the same sweep also accumulates
+// w_i = sum_j 2^(a_t)(a_t - a_s), a_m = c z_m - ref_m, so that with
+// L_m = sum_j 2^(a_m) (log2 units throughout)
+//   KL_i / ln2 = sum_j r_t (log2 r_t - log2 r_s) = w_i / L_t + log2(L_s / L_t),
+// because log2 r_m = a_m - log2 L_m.  The loss then costs 2 GEMM-units
+// instead of phase 1 plus a phase-2 sweep.  Identical inputs give a_t == a_s
+// and L_t == L_s bit for bit, hence exactly zero.
+template <int D, bool KL>
 __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, int nblk) {
   constexpr int KS = D / 16, RB = 2 * D, TB = Tile<D>::BYTES;
   __shared__ __attribute__((aligned(1024))) char lds[2][2][TB];
@@ -301,7 +330,7 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, 
   ns += __shfl_xor(ns, 32);
   const float ref_t = nt * c, ref_s = ns * c;
 
-  double lsum_t = 0.0, lsum_s = 0.0;
+  double lsum_t = 0.0, lsum_s = 0.0, wkl = 0.0;
   Tile<D>::load(lds[0][0], xt, 0, n, wave, lane);
   Tile<D>::load(lds[0][1], xs, 0, n, wave, lane);
   for (int tI = 0; tI < ntiles; ++tI) {
@@ -319,19 +348,23 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, 
       f32x16 St, Ss;
       logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
       if (need_mask)
-        lse_block_fixed<true>(St, Ss, c, ref_t, ref_s, sw0 + 32 * sb, i, n, a.causal, h, lsum_t, lsum_s);
+        lse_block_fixed<true, KL>(St, Ss, c, ref_t, ref_s, sw0 + 32 * sb, i, n, a.causal, h, lsum_t, lsum_s, wkl);
       else
-        lse_block_fixed<false>(St, Ss, c, ref_t, ref_s, sw0 + 32 * sb, i, n, a.causal, h, lsum_t, lsum_s);
+        lse_block_fixed<false, KL>(St, Ss, c, ref_t, ref_s, sw0 + 32 * sb, i, n, a.causal, h, lsum_t, lsum_s, wkl);
     }
   }
   lsum_t += __shfl_xor(lsum_t, 32);
   lsum_s += __shfl_xor(lsum_s, 32);
-  const bool bad = i < n && !(lsum_t > 0.0 && lsum_t < 1e300 && lsum_s > 0.0 && lsum_s < 1e300);
+  if (KL) wkl += __shfl_xor(wkl, 32);
+  const bool bad = i < n && !(lsum_t > 0.0 && lsum_t < 1e300 && lsum_s > 0.0 && lsum_s < 1e300 &&
+                              (!KL || fabs(wkl) < 1e300));
   if (!__syncthreads_or(bad)) {
     // LSE = ln2 * (ref + log2 L), in fp64.
     if (h == 0 && i < n) {
-      static_cast<double*>(a.lse_t)[bh * n + i] = ((double)ref_t + log2(lsum_t)) * kLn2D;
-      static_cast<double*>(a.lse_s)[bh * n + i] = ((double)ref_s + log2(lsum_s)) * kLn2D;
+      const double l2t = log2(lsum_t), l2s = log2(lsum_s);
+      static_cast<double*>(a.lse_t)[bh * n + i] = ((double)ref_t + l2t) * kLn2D;
+      static_cast<double*>(a.lse_s)[bh * n + i] = ((double)ref_s + l2s) * kLn2D;
+      if (KL) a.row_kl[bh * n + i] = (float)((wkl / lsum_t + (l2s - l2t)) * kLn2D);
     }
     return;
   }
@@ -363,10 +396,36 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, 
   // is evaluated in fp64 so the combination adds no fp32 rounding.
   const double Lt = lsum_t * exp2((double)fmaf(mt, c, -Mct)) + lt2 * exp2((double)fmaf(mt2, c, -Mct));
   const double Ls = lsum_s * exp2((double)fmaf(ms, c, -Mcs)) + ls2 * exp2((double)fmaf(ms2, c, -Mcs));
+  const double L2t = (double)Mct + log2(Lt), L2s = (double)Mcs + log2(Ls);
   if (h == 0 && i < n) {
-    static_cast<double*>(a.lse_t)[bh * n + i] = ((double)Mct + log2(Lt)) * kLn2D;
-    static_cast<double*>(a.lse_s)[bh * n + i] = ((double)Mcs + log2(Ls)) * kLn2D;
+    static_cast<double*>(a.lse_t)[bh * n + i] = L2t * kLn2D;
+    static_cast<double*>(a.lse_s)[bh * n + i] = L2s * kLn2D;
   }
+  if (!KL) return;
+  // KL after the fallback: a second sweep against the exact statistics,
+  // as the phase-2 row sweep forms it:
+  //   KL_i = ln2 * (2^-lo_t * sum_j 2^(a_t)(a_t - a_s) + lo_s - lo_t),
+  // a_m = c z_m - hi_m, hi_m the fp32 rounding of L2_m and lo_m the rest.
+  const float ht = (float)L2t, hs = (float)L2s;
+  const double lot = L2t - (double)ht, los = L2s - (double)hs;
+  double kacc = 0.0;
+  for (int tI = 0; tI < ntiles; ++tI) {
+    const int buf = tI & 1, sw0 = tI * kSW;
+    __syncthreads();
+    Tile<D>::load(lds[buf][0], xt, sw0, n, wave, lane);
+    Tile<D>::load(lds[buf][1], xs, sw0, n, wave, lane);
+    wait_loads();
+    __syncthreads();
+    if (a.causal && sw0 > wown0 + 31) continue;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x16 St, Ss;
+      logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
+      kl_block_stat(St, Ss, c, ht, hs, sw0 + 32 * sb, i, n, a.causal, h, kacc);
+    }
+  }
+  kacc += __shfl_xor(kacc, 32);
+  if (h == 0 && i < n) a.row_kl[bh * n + i] = (float)((exp2(-lot) * kacc + los - lot) * kLn2D);
 }
 
 // ---------------------------------------------------------------------------
@@ -707,10 +766,10 @@ __global__ void zero_scalar_kernel(float* p) { *p = 0.f; }
 // ---------------------------------------------------------------------------
 inline int blocks_per_head(int n) { return (n + kOwn - 1) / kOwn; }
 
-template <int D>
+template <int D, bool KL>
 hipError_t lse_typed(const SweepArgs& a, hipStream_t st) {
   const int nb = blocks_per_head(a.n);
-  hipLaunchKernelGGL((lse_fwd_kernel<D>), dim3((unsigned)(nb * a.bh)), dim3(kNT), 0, st, a, nb);
+  hipLaunchKernelGGL((lse_fwd_kernel<D, KL>), dim3((unsigned)(nb * a.bh)), dim3(kNT), 0, st, a, nb);
   return hipGetLastError();
 }
 
@@ -729,7 +788,19 @@ hipError_t sweep_typed(const SweepArgs& a, hipStream_t st) {
 
 hipError_t launch_lse_fwd(const SweepArgs& a, hipStream_t st) {
   if (a.fp32) return launch_wide_lse_fwd(a, st);
-  return a.d == 64 ? lse_typed<64>(a, st) : lse_typed<128>(a, st);
+  return a.d == 64 ? lse_typed<64, false>(a, st) : lse_typed<128, false>(a, st);
+}
+
+hipError_t launch_kl_fwd(const SweepArgs& a, hipStream_t st) {
+  if (a.fp32) {
+    // Precision mode: the fp64 phase-1 and row-KL kernels, without gradient.
+    hipError_t e = launch_wide_lse_fwd(a, st);
+    if (e != hipSuccess) return e;
+    SweepArgs b = a;
+    b.dx = nullptr;
+    return launch_wide_kl_row(b, st);
+  }
+  return a.d == 64 ? lse_typed<64, true>(a, st) : lse_typed<128, true>(a, st);
 }
 
 hipError_t launch_kl_row(const SweepArgs& a, hipStream_t st) {

@@ -11,9 +11,9 @@ namespace lmr {
 struct SweepArgs {
   const void* xt;        // [BH, n, d] teacher, bf16 bits or fp32
   const void* xs;        // [BH, n, d] student
-  void* lse_t;           // [BH, n] fp32 (bf16 inputs) or fp64 (fp32 inputs)
+  void* lse_t;           // [BH, n] fp64, natural log
   void* lse_s;           // [BH, n]
-  float* row_kl;         // [BH, n]  phase-2 output (may be null for COL sweeps)
+  float* row_kl;         // [BH, n]  row KL output (may be null for COL sweeps)
   float* dx;             // [BH, n, d] fp32 gradient (null = no gradient)
   int64_t bh;            // number of heads B*H
   int n;                 // sequence length
@@ -26,6 +26,8 @@ struct SweepArgs {
 };
 
 hipError_t launch_lse_fwd(const SweepArgs& a, hipStream_t st);
+// Phase 1 with the KL accumulator: LSE_t, LSE_s and row_kl in one sweep.
+hipError_t launch_kl_fwd(const SweepArgs& a, hipStream_t st);
 // Row-owned phase-2 sweep: row KL and the row term dZ X_s (stored, not added).
 hipError_t launch_kl_row(const SweepArgs& a, hipStream_t st);
 // Column-owned phase-2 sweep: adds the column term dZ^T X_s into dx.

@@ -86,6 +86,26 @@ def test_empty_sequence_is_a_noop(lib):
     assert st == 0
 
 
+def _fwd(lib, **kw):
+    a = dict(xt=FAKE, xs=FAKE, dt=0, B=1, H=2, n=64, d=128, scale=0.1, causal=1, lt=FAKE, ls=FAKE, rk=FAKE)
+    a.update(kw)
+    return lib.larard_kl_fwd(a["xt"], a["xs"], a["dt"], a["B"], a["H"], a["n"], a["d"], a["scale"],
+                             a["causal"], a["lt"], a["ls"], a["rk"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rk=None), 1), (dict(rk=FAKE + 2), 1), (dict(lt=None), 1), (dict(ls=FAKE + 4), 1),
+    (dict(xs=None), 1), (dict(d=80), 2), (dict(dt=3), 2), (dict(scale=0.0), 1), (dict(B=0), 1),
+])
+def test_kl_fwd_validation(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+    assert lib.larard_last_error().decode() != ""
+
+
+def test_kl_fwd_empty_sequence_is_a_noop(lib):
+    assert _fwd(lib, n=0, xt=None, xs=None, lt=None, ls=None, rk=None) == 0
+
+
 def _bwd(lib, **kw):
     a = dict(xt=FAKE, xs=FAKE, dt=0, B=1, H=2, n=64, d=64, scale=0.1, causal=1, lt=FAKE, ls=FAKE,
              lscale=1.0, rk=FAKE, dx=FAKE, mode=0)

@@ -83,5 +83,20 @@ def test_full_size_sampled(gpu_lib, name):
                 full = oracle.relation_kl_head(a64, b64, s, True)["loss"]
                 got_h = float(row_kl[b, h].double().sum() / n)
                 assert abs(got_h - full) / abs(full) < 1e-3, (got_h, full)
-        del xt, xs, dx, ws
+        # Forward-only sweep on the same inputs: its LSE equals phase 1's
+        # (same sums in the same order), its row KL agrees with phase 2's at
+        # the per-row KL bound on every row, and sampled rows match the oracle.
+        f_lt, f_ls, f_kl = gpu_lib.kl_fwd(xt, xs, w.scale, True)
+        torch.cuda.synchronize()
+        assert torch.equal(f_lt, lse_t) and torch.equal(f_ls, lse_s)
+        zall = w.scale * max(float(np.max(np.sum(m.xt64 ** 2, -1))), float(np.max(np.sum(m.xs64 ** 2, -1))))
+        kl_bound = 2e-6 + 1e-4 * float(row_kl.abs().max()) + 8 * EPS32 * zall
+        d_kl = float((f_kl - row_kl).abs().max())
+        print(f"  {mname}/{mname} forward-only: max |row_kl - phase-2 row_kl| = {d_kl:.2e}", flush=True)
+        assert d_kl < 2 * kl_bound
+        b0, h0 = heads[0]
+        rows0 = _rows(n, rng)
+        a64, b64 = m.head64(b0, h0)
+        assert np.max(np.abs(f_kl[b0, h0].cpu().numpy()[rows0] - oracle.row_kl_rows(a64, b64, s, rows0))) < kl_bound
+        del xt, xs, dx, ws, f_lt, f_ls, f_kl
         torch.cuda.empty_cache()

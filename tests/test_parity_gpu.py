@@ -161,13 +161,92 @@ def test_growing_logits_exercise_online_rescaling(gpu_lib):
 
 
 def test_loss_only_matches_full(gpu_lib):
+    # Loss only runs the one-sweep forward path; the full path forms the KL in
+    # phase 2.  Both are checked against the oracle, and against each other at
+    # the per-row KL bound.
     import torch
     xt, xs = random_pair(1, 2, 190, 128, 0.3, seed=4)
     a, b = to_device(xt, "bf16"), to_device(xs, "bf16")
+    s = 1.0 / np.sqrt(128)
     l1, _ = gpu_lib.loss(a, b, need_dx=False)
     l2, _ = gpu_lib.loss(a, b, need_dx=True)
     torch.cuda.synchronize()
-    assert float(l1.cpu()) == float(l2.cpu())
+    ref = oracle.relation_kl(widen(xt, "bf16"), widen(xs, "bf16"), f32(s), True)["loss"]
+    assert rel(float(l1.cpu()), ref) < TOL["bf16"]["loss"]
+    assert rel(float(l2.cpu()), ref) < TOL["bf16"]["loss"]
+    zmax = _logit_bound(widen(xt, "bf16"), widen(xs, "bf16"), s)
+    assert abs(float(l1.cpu()) - float(l2.cpu())) < 2 * (TOL["bf16"]["kl"] + 8 * EPS32 * zmax) * 2
+
+
+def _fwd_compare(got_lt, got_ls, got_kl, ref, dtype, zmax):
+    tol = TOL[dtype]
+    scale_err = (EPS32 * zmax * 8) if dtype == "bf16" else 0.0
+    for g, k in ((got_lt, "lse_t"), (got_ls, "lse_s")):
+        err = np.max(np.abs(g - ref[k]))
+        assert err < tol["lse"] * (1 + np.max(np.abs(ref[k]))) + scale_err, (k, err)
+    kl_err = np.max(np.abs(got_kl - ref["row_kl"]))
+    assert kl_err < tol["kl"] + 1e-4 * np.max(np.abs(ref["row_kl"])) + scale_err, kl_err
+
+
+def _run_fwd(lmr, xt_np, xs_np, dtype, scale, causal=True):
+    import torch
+    xt, xs = to_device(xt_np, dtype), to_device(xs_np, dtype)
+    lt, ls, kl = lmr.kl_fwd(xt, xs, scale, causal)
+    torch.cuda.synchronize()
+    return lt.cpu().numpy(), ls.cpu().numpy(), kl.cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 129, 200, 333])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_kl_fwd_ragged(gpu_lib, n, d, causal):
+    """Forward-only sweep: LSE and row KL in one pass against the dense oracle."""
+    xt, xs = random_pair(1, 2, n, d, 0.4, seed=n * 3 + d + causal)
+    s = 1.0 / np.sqrt(d)
+    a, b = widen(xt, "bf16"), widen(xs, "bf16")
+    ref = oracle.relation_kl(a, b, f32(s), causal)
+    _fwd_compare(*_run_fwd(gpu_lib, xt, xs, "bf16", s, causal), ref, "bf16", _logit_bound(a, b, s))
+
+
+@pytest.mark.parametrize("n", [1, 100, 257])
+def test_kl_fwd_fp32(gpu_lib, n):
+    xt, xs = random_pair(2, 1, n, 64, 0.4, seed=40 + n, dtype="f32")
+    s = 1.0 / 8.0
+    a, b = widen(xt, "f32"), widen(xs, "f32")
+    ref = oracle.relation_kl(a, b, f32(s), True)
+    _fwd_compare(*_run_fwd(gpu_lib, xt, xs, "f32", s), ref, "f32", _logit_bound(a, b, s))
+
+
+def test_kl_fwd_identical_inputs_give_exact_zero(gpu_lib):
+    xt, _ = random_pair(1, 3, 260, 128, 0.0, seed=13)
+    lt, ls, kl = _run_fwd(gpu_lib, xt, xt.copy(), "bf16", 1 / np.sqrt(128))
+    assert np.all(kl == 0.0) and np.array_equal(lt, ls)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_kl_fwd_overflowing_shift_takes_the_exact_fallback(gpu_lib, causal):
+    n, d = 150, 64
+    rng = np.random.default_rng(12)
+    xt = rng.standard_normal((1, 2, n, d))
+    xt[:, :, 3] *= 30.0
+    xs = xt + 0.3 * rng.standard_normal((1, 2, n, d))
+    xt, xs = si.round_bf16_bits(xt), si.round_bf16_bits(xs)
+    got = _run_fwd(gpu_lib, xt, xs, "bf16", 0.125, causal)
+    a, b = widen(xt, "bf16"), widen(xs, "bf16")
+    ref = oracle.relation_kl(a, b, 0.125, causal)
+    assert all(np.all(np.isfinite(g)) for g in got)
+    _fwd_compare(*got, ref, "bf16", _logit_bound(a, b, 0.125))
+
+
+def test_kl_fwd_peaky_heads(gpu_lib):
+    # Per-head projection scales as in the GQA workload: some rows put almost
+    # all probability on the diagonal.
+    w = si.workload("llama3_gqa_8k", n=384, B=1)
+    m = si.make_inputs(w, maps=["K"])["K"]
+    a, b = m.xt64[:, :4], m.xs64[:, :4]
+    got = _run_fwd(gpu_lib, np.ascontiguousarray(m.xt[:, :4]), np.ascontiguousarray(m.xs[:, :4]), "bf16", w.scale)
+    ref = oracle.relation_kl(a, b, f32(w.scale), True)
+    _fwd_compare(*got, ref, "bf16", _logit_bound(a, b, w.scale))
 
 
 def test_split_mode_is_bitwise_deterministic(gpu_lib):
