@@ -331,6 +331,37 @@ def main():
     ms_fwd = s3.elapsed_time(e3) / args.steps
     losses_fwd = {b["name"]: float(b["loss"].cpu()) for b in bufs}
 
+    # General relation X != Y on the same data: the query/key map (X = Q,
+    # Y = K), fwd+bwd through one larard_xy_loss call (dX_s and dY_s).
+    cross = None
+    names = [b["name"] for b in bufs]
+    if "Q" in names and "K" in names:
+        bq, bk = bufs[names.index("Q")], bufs[names.index("K")]
+        if bq["xt"].shape == bk["xt"].shape:
+            wsx = torch.empty(lmr.workspace_bytes(bq["B"], bq["H"], bq["n"]), dtype=torch.uint8, device=dev)
+            dyq = torch.empty_like(bq["dx"])
+
+            def cross_step():
+                lmr.xy_loss(bq["xt"], bq["xs"], bk["xt"], bk["xs"], scale, True, 1.0, workspace=wsx,
+                            out=bq["loss"], dx=bq["dx"], dy=dyq)
+            for _ in range(args.warmup):
+                cross_step()
+            torch.cuda.synchronize()
+            s4, e4 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s4.record()
+            for _ in range(args.steps):
+                cross_step()
+            e4.record()
+            torch.cuda.synchronize()
+            ms_x = s4.elapsed_time(e4) / args.steps
+            cross = {"ms_per_map": round(ms_x, 4),
+                     "tflops": round(6 * units(bq) / (ms_x * 1e-3) / 1e12, 3),
+                     "pct_bf16_peak": round(100 * 6 * units(bq) / (ms_x * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     "loss": float(bq["loss"].cpu()),
+                     "what": "query/key relation (X=Q, Y=K) via larard_xy_loss: LSE, row KL, dX_s and dY_s; "
+                             "6 GEMM-units per head"}
+            del wsx, dyq
+
     # Algorithmic work.  Per head-map P = n(n+1)/2 unmasked pairs, one
     # contraction = 2*d*P flops.  Phase 1: 2 contractions; the row sweep
     # carries phase 2's recompute (2) and the row term (1); the column sweep's
@@ -390,6 +421,7 @@ def main():
                                                 / PEAK_BF16_TFLOPS, 2),
                          "losses": losses_fwd,
                          "what": "larard_kl_fwd + reduce per map; algorithmic flops 2 GEMM-units per head-map"},
+        "cross_relation": cross,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, maps, args.cpu_sample_n)

@@ -152,6 +152,51 @@ larard_status larard_loss(const void* x_t, const void* x_s, larard_dtype dtype,
                           void* workspace, size_t workspace_bytes,
                           float* loss, float* dx_s, int dx_mode, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * General relation X != Y (notes page, "Key designs" item 1 defines the map
+ * for projected sequences X_m, Y_m; item 3 contracts dZ into both dX_s and
+ * dY_s).  For each head:
+ *     Z_m = scale * X_m Y_m^T   (rows i from X, columns j from Y; causal keeps j <= i)
+ *     R_m = row-softmax(Z_m),   loss = (1/n) sum_i KL(R_t(i,:) || R_s(i,:))
+ *     dX_s = loss_scale * scale * dZ Y_s,   dY_s = loss_scale * scale * dZ^T X_s,
+ *     dZ = (R_s - R_t)/n,
+ * e.g. the query/key attention map (X = Q, Y = K).  y_t, y_s are [B,H,n,d]
+ * device tensors of the same dtype and layout as x_t, x_s (16-byte aligned);
+ * every other convention is that of the self-relation calls above.  Passing
+ * y = x gives dX_s + dY_s = the self-relation gradient.
+ * ------------------------------------------------------------------------- */
+
+/* Phase 1 of the X/Y relation: lse_t, lse_s over the rows of Z (fp64 [B,H,n]). */
+larard_status larard_xy_lse_fwd(const void* x_t, const void* x_s, const void* y_t, const void* y_s,
+                                larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d,
+                                float scale, int causal, void* lse_t, void* lse_s, void* stream);
+
+/* Forward-only X/Y relation: lse_t, lse_s and row_kl in one sweep (as
+ * larard_kl_fwd).  All outputs required. */
+larard_status larard_xy_kl_fwd(const void* x_t, const void* x_s, const void* y_t, const void* y_s,
+                               larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d,
+                               float scale, int causal, void* lse_t, void* lse_s, float* row_kl,
+                               void* stream);
+
+/* Phase 2 of the X/Y relation (split mode): row_kl (required) and the
+ * gradients dx_s and dy_s (fp32 [B,H,n,d], OVERWRITTEN; either may be NULL
+ * to skip it).  lse_t / lse_s must come from larard_xy_lse_fwd (or
+ * larard_xy_kl_fwd) with the same inputs. */
+larard_status larard_xy_kl_bwd(const void* x_t, const void* x_s, const void* y_t, const void* y_s,
+                               larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d,
+                               float scale, int causal, const void* lse_t, const void* lse_s,
+                               float loss_scale, float* row_kl, float* dx_s, float* dy_s,
+                               void* stream);
+
+/* Whole X/Y path for one relation map with the workspace of larard_loss
+ * (same size and layout).  dx_s == dy_s == NULL computes the loss only,
+ * in one sweep. */
+larard_status larard_xy_loss(const void* x_t, const void* x_s, const void* y_t, const void* y_s,
+                             larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d,
+                             float scale, int causal, float loss_scale,
+                             void* workspace, size_t workspace_bytes,
+                             float* loss, float* dx_s, float* dy_s, void* stream);
+
 /* Byte offsets of the regions larard_loss carves from its workspace:
  * off[0] = lse_t, off[1] = lse_s, off[2] = row_kl, off[3] = fp64 partials.
  * Returns LARARD_E_INVALID for invalid sizes. */

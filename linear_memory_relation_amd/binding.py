@@ -59,6 +59,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.larard_loss.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, f32, vp, ctypes.c_size_t,
                                 vp, vp, i32, vp]
     lib.larard_loss.restype = i32
+    lib.larard_xy_lse_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, vp]
+    lib.larard_xy_lse_fwd.restype = i32
+    lib.larard_xy_kl_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, vp, vp]
+    lib.larard_xy_kl_fwd.restype = i32
+    lib.larard_xy_kl_bwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, f32, vp, vp, vp, vp]
+    lib.larard_xy_kl_bwd.restype = i32
+    lib.larard_xy_loss.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, f32, i32, f32, vp, ctypes.c_size_t,
+                                   vp, vp, vp, vp]
+    lib.larard_xy_loss.restype = i32
     lib.larard_status_str.argtypes = [i32]
     lib.larard_status_str.restype = ctypes.c_char_p
     lib.larard_last_error.argtypes = []
@@ -221,6 +230,78 @@ def loss(xt: torch.Tensor, xs: torch.Tensor, scale: Optional[float] = None, caus
                             _ptr(out), _ptr(dx), int(dx_mode), _stream())
     _check(st, "larard_loss")
     return out, dx
+
+
+# ---------------------------------------------------------------------------
+# General relation X != Y: Z = scale * X Y^T, gradients dX_s and dY_s.
+# ---------------------------------------------------------------------------
+def _shape_xy(xt, xs, yt, ys):
+    shp = _shape(xt, xs)
+    if _shape(yt, ys) != shp or yt.dtype != xt.dtype:
+        raise ValueError("y_t, y_s must match x_t, x_s in shape and dtype")
+    return shp
+
+
+def xy_lse_fwd(xt, xs, yt, ys, scale=None, causal=True, lse_t=None, lse_s=None):
+    """Phase 1 of the X/Y relation: (lse_t, lse_s), fp64 [B, H, n]."""
+    B, H, n, d = _shape_xy(xt, xs, yt, ys)
+    scale = default_scale(d) if scale is None else float(scale)
+    lse_t = torch.empty((B, H, n), dtype=torch.float64, device=xt.device) if lse_t is None else lse_t
+    lse_s = torch.empty((B, H, n), dtype=torch.float64, device=xt.device) if lse_s is None else lse_s
+    st = load().larard_xy_lse_fwd(_ptr(xt), _ptr(xs), _ptr(yt), _ptr(ys), _dtype_code(xt), B, H, n, d, scale,
+                                  int(causal), _ptr(lse_t), _ptr(lse_s), _stream())
+    _check(st, "larard_xy_lse_fwd")
+    return lse_t, lse_s
+
+
+def xy_kl_fwd(xt, xs, yt, ys, scale=None, causal=True, lse_t=None, lse_s=None, row_kl=None):
+    """Forward-only X/Y relation in one sweep: (lse_t, lse_s, row_kl)."""
+    B, H, n, d = _shape_xy(xt, xs, yt, ys)
+    scale = default_scale(d) if scale is None else float(scale)
+    lse_t = torch.empty((B, H, n), dtype=torch.float64, device=xt.device) if lse_t is None else lse_t
+    lse_s = torch.empty((B, H, n), dtype=torch.float64, device=xt.device) if lse_s is None else lse_s
+    row_kl = torch.empty((B, H, n), dtype=torch.float32, device=xt.device) if row_kl is None else row_kl
+    st = load().larard_xy_kl_fwd(_ptr(xt), _ptr(xs), _ptr(yt), _ptr(ys), _dtype_code(xt), B, H, n, d, scale,
+                                 int(causal), _ptr(lse_t), _ptr(lse_s), _ptr(row_kl), _stream())
+    _check(st, "larard_xy_kl_fwd")
+    return lse_t, lse_s, row_kl
+
+
+def xy_kl_bwd(xt, xs, yt, ys, lse_t, lse_s, scale=None, causal=True, loss_scale=1.0, need_dx=True,
+              need_dy=True, row_kl=None, dx=None, dy=None):
+    """Phase 2 of the X/Y relation: (row_kl, dX_s or None, dY_s or None)."""
+    B, H, n, d = _shape_xy(xt, xs, yt, ys)
+    scale = default_scale(d) if scale is None else float(scale)
+    row_kl = torch.empty((B, H, n), dtype=torch.float32, device=xt.device) if row_kl is None else row_kl
+    dx = (torch.empty((B, H, n, d), dtype=torch.float32, device=xt.device) if dx is None else dx) if need_dx else None
+    dy = (torch.empty((B, H, n, d), dtype=torch.float32, device=xt.device) if dy is None else dy) if need_dy else None
+    st = load().larard_xy_kl_bwd(_ptr(xt), _ptr(xs), _ptr(yt), _ptr(ys), _dtype_code(xt), B, H, n, d, scale,
+                                 int(causal), _ptr(lse_t), _ptr(lse_s), float(loss_scale), _ptr(row_kl),
+                                 _ptr(dx), _ptr(dy), _stream())
+    _check(st, "larard_xy_kl_bwd")
+    return row_kl, dx, dy
+
+
+def xy_loss(xt, xs, yt, ys, scale=None, causal=True, loss_scale=1.0, need_grad=True, workspace=None,
+            out=None, dx=None, dy=None):
+    """Whole X/Y path for one relation map: (loss 0-d fp32 tensor, dX_s or None, dY_s or None)."""
+    B, H, n, d = _shape_xy(xt, xs, yt, ys)
+    scale = default_scale(d) if scale is None else float(scale)
+    nbytes = workspace_bytes(B, H, n, _dtype_code(xt))
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=xt.device)
+    out = torch.empty((), dtype=torch.float32, device=xt.device) if out is None else out
+    if need_grad:
+        dx = torch.empty((B, H, n, d), dtype=torch.float32, device=xt.device) if dx is None else dx
+        dy = torch.empty((B, H, n, d), dtype=torch.float32, device=xt.device) if dy is None else dy
+    else:
+        dx = dy = None
+    st = load().larard_xy_loss(_ptr(xt), _ptr(xs), _ptr(yt), _ptr(ys), _dtype_code(xt), B, H, n, d, scale,
+                               int(causal), float(loss_scale), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _ptr(out), _ptr(dx), _ptr(dy),
+                               _stream())
+    _check(st, "larard_xy_loss")
+    return out, dx, dy
 
 
 def version() -> str:

@@ -66,6 +66,9 @@ lmr::SweepArgs make_args(const void* x_t, const void* x_s, larard_dtype dtype, i
   lmr::SweepArgs a{};
   a.xt = x_t;
   a.xs = x_s;
+  a.yt = x_t;            // self-relation unless set_cross() replaces Y
+  a.ys = x_s;
+  a.cross = 0;
   a.bh = B * H;
   a.n = (int)n;
   a.d = (int)d;
@@ -73,6 +76,18 @@ lmr::SweepArgs make_args(const void* x_t, const void* x_s, larard_dtype dtype, i
   a.causal = causal ? 1 : 0;
   a.scale = scale;
   return a;
+}
+
+// Cross relation: Y tensors of the same shape and dtype as X.
+larard_status set_cross(lmr::SweepArgs* a, const void* y_t, const void* y_s, int64_t n) {
+  if (n > 0) {
+    if (y_t == nullptr || y_s == nullptr) return fail(LARARD_E_INVALID, "y_t / y_s must not be NULL");
+    if (!aligned(y_t, 16) || !aligned(y_s, 16)) return fail(LARARD_E_INVALID, "y_t / y_s must be 16-byte aligned");
+  }
+  a->yt = y_t;
+  a->ys = y_s;
+  a->cross = 1;
+  return LARARD_OK;
 }
 
 larard_status check_dx_mode(int dx_mode) {
@@ -87,7 +102,7 @@ larard_status run_kl_bwd(lmr::SweepArgs a, float loss_scale, hipStream_t st) {
   a.grad_scale_d = (double)loss_scale * (double)a.scale / (double)a.n;
   hipError_t e = lmr::launch_kl_row(a, st);
   if (e != hipSuccess) return hip_fail(e, "kl_bwd row sweep launch");
-  if (a.dx != nullptr) {
+  if ((a.cross ? a.dy : a.dx) != nullptr) {
     e = lmr::launch_kl_col(a, st);
     if (e != hipSuccess) return hip_fail(e, "kl_bwd column sweep launch");
   }
@@ -273,6 +288,105 @@ larard_status larard_reduce_loss(const float* row_kl, int64_t B, int64_t H, int6
   if (partials == nullptr || !aligned(partials, 8)) return fail(LARARD_E_INVALID, "partials must be an 8-byte aligned pointer");
   const hipError_t e = lmr::launch_reduce(row_kl, B * H, (int)n, loss_scale, partials, loss, st);
   return e == hipSuccess ? LARARD_OK : hip_fail(e, "loss reduction launch");
+}
+
+// ---------------------------------------------------------------------------
+// General relation X != Y (larard.h, "cross relation" entry points).
+// ---------------------------------------------------------------------------
+larard_status larard_xy_lse_fwd(const void* x_t, const void* x_s, const void* y_t, const void* y_s,
+                                larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d, float scale,
+                                int causal, void* lse_t, void* lse_s, void* stream) {
+  larard_status s = check_common(x_t, x_s, dtype, B, H, n, d, scale);
+  if (s != LARARD_OK) return s;
+  lmr::SweepArgs a = make_args(x_t, x_s, dtype, B, H, n, d, scale, causal);
+  if ((s = set_cross(&a, y_t, y_s, n)) != LARARD_OK || n == 0) return s;
+  if (lse_t == nullptr || lse_s == nullptr) return fail(LARARD_E_INVALID, "lse_t / lse_s must not be NULL");
+  if (!aligned(lse_t, stat_bytes(dtype)) || !aligned(lse_s, stat_bytes(dtype)))
+    return fail(LARARD_E_INVALID, "lse buffers must be aligned to their element size");
+  a.lse_t = lse_t;
+  a.lse_s = lse_s;
+  const hipError_t e = lmr::launch_lse_fwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LARARD_OK : hip_fail(e, "xy_lse_fwd launch");
+}
+
+larard_status larard_xy_kl_fwd(const void* x_t, const void* x_s, const void* y_t, const void* y_s,
+                               larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d, float scale,
+                               int causal, void* lse_t, void* lse_s, float* row_kl, void* stream) {
+  larard_status s = check_common(x_t, x_s, dtype, B, H, n, d, scale);
+  if (s != LARARD_OK) return s;
+  lmr::SweepArgs a = make_args(x_t, x_s, dtype, B, H, n, d, scale, causal);
+  if ((s = set_cross(&a, y_t, y_s, n)) != LARARD_OK || n == 0) return s;
+  if (lse_t == nullptr || lse_s == nullptr) return fail(LARARD_E_INVALID, "lse_t / lse_s must not be NULL");
+  if (!aligned(lse_t, stat_bytes(dtype)) || !aligned(lse_s, stat_bytes(dtype)))
+    return fail(LARARD_E_INVALID, "lse buffers must be aligned to their element size");
+  if (row_kl == nullptr || !aligned(row_kl, 4)) return fail(LARARD_E_INVALID, "row_kl must be a 4-byte aligned pointer");
+  a.lse_t = lse_t;
+  a.lse_s = lse_s;
+  a.row_kl = row_kl;
+  const hipError_t e = lmr::launch_kl_fwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LARARD_OK : hip_fail(e, "xy_kl_fwd launch");
+}
+
+larard_status larard_xy_kl_bwd(const void* x_t, const void* x_s, const void* y_t, const void* y_s,
+                               larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d, float scale,
+                               int causal, const void* lse_t, const void* lse_s, float loss_scale,
+                               float* row_kl, float* dx_s, float* dy_s, void* stream) {
+  lmr::SweepArgs a;
+  larard_status s = check_phase2(x_t, x_s, dtype, B, H, n, d, scale, causal, lse_t, lse_s, loss_scale, &a);
+  if (s != LARARD_OK) return s;
+  if (n == 0) return set_cross(&a, y_t, y_s, n);
+  if ((s = set_cross(&a, y_t, y_s, n)) != LARARD_OK) return s;
+  if (row_kl == nullptr || !aligned(row_kl, 4)) return fail(LARARD_E_INVALID, "row_kl must be a 4-byte aligned pointer");
+  if ((dx_s != nullptr && !aligned(dx_s, 16)) || (dy_s != nullptr && !aligned(dy_s, 16)))
+    return fail(LARARD_E_INVALID, "dx_s / dy_s must be 16-byte aligned");
+  a.row_kl = row_kl;
+  a.dx = dx_s;
+  a.dy = dy_s;
+  return run_kl_bwd(a, loss_scale, static_cast<hipStream_t>(stream));
+}
+
+larard_status larard_xy_loss(const void* x_t, const void* x_s, const void* y_t, const void* y_s,
+                             larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d, float scale,
+                             int causal, float loss_scale, void* workspace, size_t workspace_bytes, float* loss,
+                             float* dx_s, float* dy_s, void* stream) {
+  larard_status s = check_common(x_t, x_s, dtype, B, H, n, d, scale);
+  if (s != LARARD_OK) return s;
+  lmr::SweepArgs a = make_args(x_t, x_s, dtype, B, H, n, d, scale, causal);
+  if ((s = set_cross(&a, y_t, y_s, n)) != LARARD_OK) return s;
+  if (!std::isfinite(loss_scale)) return fail(LARARD_E_INVALID, "loss_scale must be finite");
+  if (loss == nullptr || !aligned(loss, 4)) return fail(LARARD_E_INVALID, "loss must be a 4-byte aligned device pointer");
+  if ((dx_s != nullptr && !aligned(dx_s, 16)) || (dy_s != nullptr && !aligned(dy_s, 16)))
+    return fail(LARARD_E_INVALID, "dx_s / dy_s must be 16-byte aligned");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n == 0) {
+    const hipError_t e = lmr::launch_zero_scalar(loss, st);
+    return e == hipSuccess ? LARARD_OK : hip_fail(e, "zero loss launch");
+  }
+  size_t off[4];
+  if ((s = larard_workspace_layout(dtype, B, H, n, off)) != LARARD_OK) return s;
+  const size_t need = larard_workspace_bytes(dtype, B, H, n);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(LARARD_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(LARARD_E_WORKSPACE, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  a.lse_t = ws + off[0];
+  a.lse_s = ws + off[1];
+  a.row_kl = reinterpret_cast<float*>(ws + off[2]);
+  double* partials = reinterpret_cast<double*>(ws + off[3]);
+  hipError_t e;
+  if (dx_s == nullptr && dy_s == nullptr) {
+    e = lmr::launch_kl_fwd(a, st);
+    if (e != hipSuccess) return hip_fail(e, "xy_kl_fwd launch");
+  } else {
+    e = lmr::launch_lse_fwd(a, st);
+    if (e != hipSuccess) return hip_fail(e, "xy_lse_fwd launch");
+    a.dx = dx_s;
+    a.dy = dy_s;
+    if ((s = run_kl_bwd(a, loss_scale, st)) != LARARD_OK) return s;
+  }
+  e = lmr::launch_reduce(a.row_kl, a.bh, a.n, loss_scale, partials, loss, st);
+  if (e != hipSuccess) return hip_fail(e, "loss reduction launch");
+  return LARARD_OK;
 }
 
 const char* larard_status_str(larard_status status) {

@@ -301,8 +301,12 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, 
   const int64_t bh = bid % a.bh;
   const int ob = nblk - 1 - (int)(bid / a.bh);          // longest rows first
   const int n = a.n;
+  // Owned rows i come from X, swept tiles (columns j) from Y (== X for a
+  // self-relation).
   const char* xt = static_cast<const char*>(a.xt) + bh * (int64_t)n * RB;
   const char* xs = static_cast<const char*>(a.xs) + bh * (int64_t)n * RB;
+  const char* yt = static_cast<const char*>(a.yt) + bh * (int64_t)n * RB;
+  const char* ys = static_cast<const char*>(a.ys) + bh * (int64_t)n * RB;
   const int own0 = ob * kOwn, wown0 = own0 + 32 * wave, i = wown0 + (lane & 31);
 
   bf16x8 Bt[KS], Bs[KS];
@@ -316,30 +320,45 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, 
   const int ntiles = last / kSW + 1;
   const float c = a.scale * kLog2e;
 
-  // Shift: c * |x_i|^2 from the row's own fragments (each lane half holds half of d).
+  // Shift: the diagonal logit c * <x_i, y_i> (c * |x_i|^2 for a self-relation),
+  // from the row's own fragments (each lane half holds half of d).
   float nt = 0.f, ns = 0.f;
+  if (a.cross) {
+    const char* qt = i < n ? yt + (int64_t)i * RB : nullptr;
+    const char* qs = i < n ? ys + (int64_t)i * RB : nullptr;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 yt8 = load_own(qt, ks, h), ys8 = load_own(qs, ks, h);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float vt = (float)Bt[ks][e], vs = (float)Bs[ks][e];
-      nt = fmaf(vt, vt, nt);
-      ns = fmaf(vs, vs, ns);
+      for (int e = 0; e < 8; ++e) {
+        nt = fmaf((float)Bt[ks][e], (float)yt8[e], nt);
+        ns = fmaf((float)Bs[ks][e], (float)ys8[e], ns);
+      }
     }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float vt = (float)Bt[ks][e], vs = (float)Bs[ks][e];
+        nt = fmaf(vt, vt, nt);
+        ns = fmaf(vs, vs, ns);
+      }
+  }
   nt += __shfl_xor(nt, 32);
   ns += __shfl_xor(ns, 32);
   const float ref_t = nt * c, ref_s = ns * c;
 
   double lsum_t = 0.0, lsum_s = 0.0, wkl = 0.0;
-  Tile<D>::load(lds[0][0], xt, 0, n, wave, lane);
-  Tile<D>::load(lds[0][1], xs, 0, n, wave, lane);
+  Tile<D>::load(lds[0][0], yt, 0, n, wave, lane);
+  Tile<D>::load(lds[0][1], ys, 0, n, wave, lane);
   for (int tI = 0; tI < ntiles; ++tI) {
     const int buf = tI & 1, sw0 = tI * kSW;
     wait_loads();
     __syncthreads();
     if (tI + 1 < ntiles) {
-      Tile<D>::load(lds[buf ^ 1][0], xt, sw0 + kSW, n, wave, lane);
-      Tile<D>::load(lds[buf ^ 1][1], xs, sw0 + kSW, n, wave, lane);
+      Tile<D>::load(lds[buf ^ 1][0], yt, sw0 + kSW, n, wave, lane);
+      Tile<D>::load(lds[buf ^ 1][1], ys, sw0 + kSW, n, wave, lane);
     }
     if (a.causal && sw0 > wown0 + 31) continue;          // tile fully above the diagonal
     const bool need_mask = (a.causal && sw0 + kSW - 1 > wown0) || (sw0 + kSW > n);
@@ -376,8 +395,8 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, 
   for (int tI = 0; tI < ntiles; ++tI) {
     const int buf = tI & 1, sw0 = tI * kSW;
     __syncthreads();
-    Tile<D>::load(lds[buf][0], xt, sw0, n, wave, lane);
-    Tile<D>::load(lds[buf][1], xs, sw0, n, wave, lane);
+    Tile<D>::load(lds[buf][0], yt, sw0, n, wave, lane);
+    Tile<D>::load(lds[buf][1], ys, sw0, n, wave, lane);
     wait_loads();
     __syncthreads();
     if (a.causal && sw0 > wown0 + 31) continue;
@@ -412,8 +431,8 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(SweepArgs a, 
   for (int tI = 0; tI < ntiles; ++tI) {
     const int buf = tI & 1, sw0 = tI * kSW;
     __syncthreads();
-    Tile<D>::load(lds[buf][0], xt, sw0, n, wave, lane);
-    Tile<D>::load(lds[buf][1], xs, sw0, n, wave, lane);
+    Tile<D>::load(lds[buf][0], yt, sw0, n, wave, lane);
+    Tile<D>::load(lds[buf][1], ys, sw0, n, wave, lane);
     wait_loads();
     __syncthreads();
     if (a.causal && sw0 > wown0 + 31) continue;
@@ -521,8 +540,13 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs 
   const int64_t bh = bid % a.bh;
   const int ob = ROLE == ROLE_ROW ? nblk - 1 - (int)(bid / a.bh) : (int)(bid / a.bh);
   const int n = a.n;
-  const char* xt = static_cast<const char*>(a.xt) + bh * (int64_t)n * RB;
-  const char* xs = static_cast<const char*>(a.xs) + bh * (int64_t)n * RB;
+  // ROW: owned rows i of X, swept rows j of Y.  COL: owned rows j of Y,
+  // swept rows i of X.  (X == Y for a self-relation.)
+  const int64_t hoff = bh * (int64_t)n * RB;
+  const char* ot = static_cast<const char*>(ROLE == ROLE_ROW ? a.xt : a.yt) + hoff;
+  const char* os = static_cast<const char*>(ROLE == ROLE_ROW ? a.xs : a.ys) + hoff;
+  const char* wt = static_cast<const char*>(ROLE == ROLE_ROW ? a.yt : a.xt) + hoff;
+  const char* ws = static_cast<const char*>(ROLE == ROLE_ROW ? a.ys : a.xs) + hoff;
   const double* glt = static_cast<const double*>(a.lse_t) + bh * n;
   const double* gls = static_cast<const double*>(a.lse_s) + bh * n;
   const int own0 = ob * kOwn, wown0 = own0 + 32 * wave, o = wown0 + (lane & 31);
@@ -530,8 +554,8 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs 
 
   bf16x8 Bt[KS], Bs[KS];
   {
-    const char* rt = o < n ? xt + (int64_t)o * RB : nullptr;
-    const char* rs = o < n ? xs + (int64_t)o * RB : nullptr;
+    const char* rt = o < n ? ot + (int64_t)o * RB : nullptr;
+    const char* rs = o < n ? os + (int64_t)o * RB : nullptr;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) { Bt[ks] = load_own(rt, ks, h); Bs[ks] = load_own(rs, ks, h); }
   }
@@ -571,8 +595,8 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs 
     lstat[b][tid] = make_float2(ht, hs);
   };
 
-  Tile<D>::load(lds[0][0], xt, t_begin * kSW, n, wave, lane);
-  Tile<D>::load(lds[0][1], xs, t_begin * kSW, n, wave, lane);
+  Tile<D>::load(lds[0][0], wt, t_begin * kSW, n, wave, lane);
+  Tile<D>::load(lds[0][1], ws, t_begin * kSW, n, wave, lane);
   if (ROLE == ROLE_COL && tid < kSW) {
     fetch_stat(t_begin);
     put_stat(0, t_begin);
@@ -583,8 +607,8 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs 
     wait_loads();
     __syncthreads();
     if (tI + 1 < t_end) {
-      Tile<D>::load(lds[buf ^ 1][0], xt, sw0 + kSW, n, wave, lane);
-      Tile<D>::load(lds[buf ^ 1][1], xs, sw0 + kSW, n, wave, lane);
+      Tile<D>::load(lds[buf ^ 1][0], wt, sw0 + kSW, n, wave, lane);
+      Tile<D>::load(lds[buf ^ 1][1], ws, sw0 + kSW, n, wave, lane);
       if (ROLE == ROLE_COL && tid < kSW) {
         put_stat(buf ^ 1, tI + 1);
         if (tI + 2 < t_end) fetch_stat(tI + 2);
@@ -686,19 +710,30 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs 
     }
   }
 
-  float corr = 0.f;                                      // ROW: -2 * sum_{j!=i} dZ(i,j) * n
+  // ROW: sum_{j!=i} dZ(i,j) * n stands in for -dZ(i,i) * n.  The diagonal
+  // entry contributes dZ(i,i) y_s[i] to dX_s[i] and dZ(i,i) x_s[i] to
+  // dY_s[i]; for a self-relation both land in dX_s.
+  float corr = 0.f;
   if (ROLE == ROLE_ROW) {
     S.kl += __shfl_xor(S.kl, 32);
     S.dsum += __shfl_xor(S.dsum, 32);
     const double klr = exp2(-(double)lot) * S.kl + (double)los - (double)lot;
     if (h == 0 && o < n && a.row_kl != nullptr) a.row_kl[bh * n + o] = (float)(klr * kLn2D);
-    corr = (float)(-2.0 * S.dsum);
+    corr = (float)((a.cross ? -1.0 : -2.0) * S.dsum);
   }
+  auto bf4 = [](const char* row, int d0, float* x4) {     // 4 bf16 of a row as fp32
+    const uint2 raw = *reinterpret_cast<const uint2*>(row + 2 * d0);
+    x4[0] = __uint_as_float(raw.x << 16);
+    x4[1] = __uint_as_float(raw.x & 0xffff0000u);
+    x4[2] = __uint_as_float(raw.y << 16);
+    x4[3] = __uint_as_float(raw.y & 0xffff0000u);
+  };
+  const float gs = a.grad_scale;
   if constexpr (WITH_DX) {
+    float* out = ROLE == ROLE_COL && a.cross ? a.dy : a.dx;
     if (o < n) {
-      float* dst = a.dx + (bh * (int64_t)n + o) * D;
-      const uint16_t* xo = reinterpret_cast<const uint16_t*>(xs + (int64_t)o * RB);
-      const float gs = a.grad_scale;
+      float* dst = out + (bh * (int64_t)n + o) * D;
+      const char* yo = ws + (int64_t)o * RB;              // ROW: y_s[i] (x_s[i] for a self-relation)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -706,9 +741,8 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs 
           const int d0 = 32 * db + 8 * g4 + 4 * h;
           f32x4 v;
           if (ROLE == ROLE_ROW) {
-            const uint2 raw = *reinterpret_cast<const uint2*>(xo + d0);   // 4 bf16 of x_s[i]
-            const float x4[4] = {__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
-                                 __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+            float x4[4];
+            bf4(yo, d0, x4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = fmaf(corr, x4[e], acc[db][4 * g4 + e]) * gs;
           } else {
@@ -719,6 +753,25 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(SweepArgs 
           if (ROLE == ROLE_ROW) *p = v;
           else *p = *p + v;
         }
+      }
+    }
+  }
+  // Cross relation: the row sweep also stores the diagonal part of dY_s[i],
+  // dZ(i,i) x_s[i]; the column sweep adds the rest.
+  if (ROLE == ROLE_ROW && a.cross && a.dy != nullptr && o < n) {
+    float* dst = a.dy + (bh * (int64_t)n + o) * D;
+    const char* xo = os + (int64_t)o * RB;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * h;
+        float x4[4];
+        bf4(xo, d0, x4);
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = corr * x4[e] * gs;
+        *reinterpret_cast<f32x4*>(dst + d0) = v;
       }
     }
   }
@@ -777,7 +830,8 @@ template <int D, int ROLE>
 hipError_t sweep_typed(const SweepArgs& a, hipStream_t st) {
   const int nb = blocks_per_head(a.n);
   const dim3 grid((unsigned)(nb * a.bh)), block(kNT);
-  if (a.dx != nullptr)
+  const bool contract = ROLE == ROLE_COL && a.cross ? a.dy != nullptr : a.dx != nullptr;
+  if (contract)
     hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, true>), grid, block, 0, st, a, nb);
   else
     hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, false>), grid, block, 0, st, a, nb);
@@ -809,9 +863,9 @@ hipError_t launch_kl_row(const SweepArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_kl_col(const SweepArgs& a, hipStream_t st) {
-  if (a.fp32) return launch_wide_kl_col(a, st);
   // The column term only exists with a gradient; without one there is nothing to do.
-  if (a.dx == nullptr) return hipSuccess;
+  if ((a.cross ? a.dy : a.dx) == nullptr) return hipSuccess;
+  if (a.fp32) return launch_wide_kl_col(a, st);
   return a.d == 64 ? sweep_typed<64, ROLE_COL>(a, st) : sweep_typed<128, ROLE_COL>(a, st);
 }
 

@@ -9,12 +9,16 @@ namespace lmr {
 
 // Geometry and arguments of one launch over B*H heads of one relation map.
 struct SweepArgs {
-  const void* xt;        // [BH, n, d] teacher, bf16 bits or fp32
-  const void* xs;        // [BH, n, d] student
+  const void* xt;        // [BH, n, d] teacher X, bf16 bits or fp32 (rows i of the relation)
+  const void* xs;        // [BH, n, d] student X
+  const void* yt;        // [BH, n, d] teacher Y (columns j); == xt for a self-relation
+  const void* ys;        // [BH, n, d] student Y; == xs for a self-relation
+  int cross;             // 1: Y != X, gradients dX_s and dY_s kept apart
   void* lse_t;           // [BH, n] fp64, natural log
   void* lse_s;           // [BH, n]
   float* row_kl;         // [BH, n]  row KL output (may be null for COL sweeps)
-  float* dx;             // [BH, n, d] fp32 gradient (null = no gradient)
+  float* dx;             // [BH, n, d] fp32 gradient dX_s (null = none); self: the whole gradient
+  float* dy;             // [BH, n, d] fp32 gradient dY_s (cross only; null = none)
   int64_t bh;            // number of heads B*H
   int n;                 // sequence length
   int d;                 // head dim (64 or 128)
@@ -28,9 +32,11 @@ struct SweepArgs {
 hipError_t launch_lse_fwd(const SweepArgs& a, hipStream_t st);
 // Phase 1 with the KL accumulator: LSE_t, LSE_s and row_kl in one sweep.
 hipError_t launch_kl_fwd(const SweepArgs& a, hipStream_t st);
-// Row-owned phase-2 sweep: row KL and the row term dZ X_s (stored, not added).
+// Row-owned phase-2 sweep: row KL and the row term dZ Y_s (stored, not
+// added); cross relations also store the diagonal part of dY_s.
 hipError_t launch_kl_row(const SweepArgs& a, hipStream_t st);
-// Column-owned phase-2 sweep: adds the column term dZ^T X_s into dx.
+// Column-owned phase-2 sweep: adds the column term dZ^T X_s into dx (self)
+// or dy (cross).
 hipError_t launch_kl_col(const SweepArgs& a, hipStream_t st);
 // fp32-input path (fp64 arithmetic on the vector ALUs), in wide.hip.
 hipError_t launch_wide_lse_fwd(const SweepArgs& a, hipStream_t st);

@@ -58,6 +58,8 @@ __global__ __launch_bounds__(WTHREADS) void wide_lse_kernel(SweepArgs a, int nbl
   const int n = a.n, i = ob * WR + r;
   const float* xt = static_cast<const float*>(a.xt) + bh * (int64_t)n * D;
   const float* xs = static_cast<const float*>(a.xs) + bh * (int64_t)n * D;
+  const float* yt = static_cast<const float*>(a.yt) + bh * (int64_t)n * D;   // swept (== x for a self-relation)
+  const float* ys = static_cast<const float*>(a.ys) + bh * (int64_t)n * D;
   float ot[KD], os[KD];
 #pragma unroll
   for (int k = 0; k < KD; ++k) {
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(WTHREADS) void wide_lse_kernel(SweepArgs a, int nbl
   double mt = -INFINITY, st = 0.0, ms = -INFINITY, ss = 0.0;
   for (int t0 = 0; t0 <= last; t0 += WT) {
     __syncthreads();
-    stage<D>(lt, ls, xt, xs, t0, n, tid);
+    stage<D>(lt, ls, yt, ys, t0, n, tid);
     __syncthreads();
     const int jend = min(t0 + WT, last + 1);
     for (int j = t0; j < jend; ++j) {
@@ -104,8 +106,13 @@ __global__ __launch_bounds__(WTHREADS) void wide_sweep_kernel(SweepArgs a, int n
   const int64_t bid = blockIdx.x, bh = bid % a.bh;
   const int ob = ROLE == WROW ? nblk - 1 - (int)(bid / a.bh) : (int)(bid / a.bh);
   const int n = a.n, o = ob * WR + r;
-  const float* xt = static_cast<const float*>(a.xt) + bh * (int64_t)n * D;
-  const float* xs = static_cast<const float*>(a.xs) + bh * (int64_t)n * D;
+  // WROW: owned rows i of X, swept rows j of Y; WCOL: owned rows j of Y,
+  // swept rows i of X (X == Y for a self-relation).
+  const int64_t hoff = bh * (int64_t)n * D;
+  const float* xt = static_cast<const float*>(ROLE == WROW ? a.xt : a.yt) + hoff;
+  const float* xs = static_cast<const float*>(ROLE == WROW ? a.xs : a.ys) + hoff;
+  const float* wt = static_cast<const float*>(ROLE == WROW ? a.yt : a.xt) + hoff;
+  const float* ws = static_cast<const float*>(ROLE == WROW ? a.ys : a.xs) + hoff;
   const double* gl_t = static_cast<const double*>(a.lse_t) + bh * n;
   const double* gl_s = static_cast<const double*>(a.lse_s) + bh * n;
   float ot[KD], os[KD];
@@ -132,7 +139,7 @@ __global__ __launch_bounds__(WTHREADS) void wide_sweep_kernel(SweepArgs a, int n
 
   for (int t0 = t_begin; t0 < t_end; t0 += WT) {
     __syncthreads();
-    stage<D>(lt, ls, xt, xs, t0, n, tid);
+    stage<D>(lt, ls, wt, ws, t0, n, tid);
     if (ROLE == WCOL && tid < WT) {
       const int g = t0 + tid;
       llt[tid] = g < n ? gl_t[g] : 0.0;
@@ -172,11 +179,13 @@ __global__ __launch_bounds__(WTHREADS) void wide_sweep_kernel(SweepArgs a, int n
   if (ROLE == WROW && q == 0 && o < n && a.row_kl != nullptr)
     a.row_kl[bh * n + o] = (float)(kl / sum_t - log(sum_t) + log(sum_s));
   if (WITH_DX && o < n) {
-    float* dst = a.dx + (bh * (int64_t)n + o) * D + q * KD;
+    // The diagonal is an ordinary entry here, so a cross relation's column
+    // sweep writes the whole of dY_s; a self-relation's adds to dX_s.
+    float* dst = (ROLE == WCOL && a.cross ? a.dy : a.dx) + (bh * (int64_t)n + o) * D + q * KD;
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
       const double v = acc[k] * a.grad_scale_d;
-      if (ROLE == WROW) dst[k] = (float)v;
+      if (ROLE == WROW || a.cross) dst[k] = (float)v;
       else dst[k] = (float)((double)dst[k] + v);
     }
   }
@@ -188,11 +197,12 @@ template <int ROLE>
 hipError_t wide_sweep(const SweepArgs& a, hipStream_t st) {
   const int nb = wide_blocks(a.n);
   const dim3 grid((unsigned)(nb * a.bh)), block(WTHREADS);
+  const bool contract = ROLE == WCOL && a.cross ? a.dy != nullptr : a.dx != nullptr;
   if (a.d == 64) {
-    if (a.dx) hipLaunchKernelGGL((wide_sweep_kernel<64, ROLE, true>), grid, block, 0, st, a, nb);
+    if (contract) hipLaunchKernelGGL((wide_sweep_kernel<64, ROLE, true>), grid, block, 0, st, a, nb);
     else hipLaunchKernelGGL((wide_sweep_kernel<64, ROLE, false>), grid, block, 0, st, a, nb);
   } else {
-    if (a.dx) hipLaunchKernelGGL((wide_sweep_kernel<128, ROLE, true>), grid, block, 0, st, a, nb);
+    if (contract) hipLaunchKernelGGL((wide_sweep_kernel<128, ROLE, true>), grid, block, 0, st, a, nb);
     else hipLaunchKernelGGL((wide_sweep_kernel<128, ROLE, false>), grid, block, 0, st, a, nb);
   }
   return hipGetLastError();

@@ -5,6 +5,6 @@ import this package.  It shares no code with the HIP library and is never on
 the product path.  See `relation_kl.py` for the definitions and citations.
 """
 from .relation_kl import (  # noqa: F401
-    relation_kl_head, relation_kl, lse_rows, row_kl_rows, dx_rows,
-    forward_only_loss,
+    relation_kl_head, relation_kl, relation_kl_xy, lse_rows, row_kl_rows, dx_rows,
+    dx_rows_xy, dy_rows_xy, forward_only_loss,
 )

@@ -129,6 +129,32 @@ def relation_kl(xt: np.ndarray, xs: np.ndarray, scale: float, causal: bool = Tru
             "row_kl": row_kl, "dxs": dxs}
 
 
+def relation_kl_xy(xt: np.ndarray, xs: np.ndarray, yt: np.ndarray, ys: np.ndarray, scale: float,
+                   causal: bool = True, loss_scale: float = 1.0) -> Dict[str, np.ndarray]:
+    """General relation Z = scale * X Y^T over a [B, H, n, d] batch (notes page,
+    "Key designs" item 1 for projected sequences X_m, Y_m; item 3 for the two
+    contractions dX_s = scale*dZ Y_s and dY_s = scale*dZ^T X_s).
+
+    Returns loss (heads summed, times loss_scale), lse_t/lse_s/row_kl [B,H,n],
+    dxs and dys [B,H,n,d] (times loss_scale), from the dense per-head definition.
+    """
+    xt, xs, yt, ys = (np.asarray(v, dtype=np.float64) for v in (xt, xs, yt, ys))
+    B, H, n, d = xt.shape
+    out = {k: np.zeros((B, H, n)) for k in ("lse_t", "lse_s", "row_kl")}
+    dxs = np.zeros((B, H, n, d))
+    dys = np.zeros((B, H, n, d))
+    loss = 0.0
+    for b in range(B):
+        for h in range(H):
+            r = relation_kl_head(xt[b, h], xs[b, h], scale, causal, yt[b, h], ys[b, h])
+            for k in ("lse_t", "lse_s", "row_kl"):
+                out[k][b, h] = r[k]
+            dxs[b, h] = r["dxs"] * loss_scale
+            dys[b, h] = r["dys"] * loss_scale
+            loss += r["loss"]
+    return {"loss": loss * loss_scale, "dxs": dxs, "dys": dys, **out}
+
+
 # ----------------------------------------------------------------------------
 # Row-sampled forms of the same definitions, for sizes where a dense n x n map
 # does not fit host memory.  Each output row is computed directly from its
@@ -149,15 +175,18 @@ def lse_rows(x: np.ndarray, scale: float, rows: Iterable[int], causal: bool = Tr
 
 
 def row_kl_rows(xt: np.ndarray, xs: np.ndarray, scale: float, rows: Iterable[int],
-                causal: bool = True) -> np.ndarray:
-    """KL(R_t(i,:) || R_s(i,:)) for the requested rows of a self-relation map."""
+                causal: bool = True, yt: Optional[np.ndarray] = None,
+                ys: Optional[np.ndarray] = None) -> np.ndarray:
+    """KL(R_t(i,:) || R_s(i,:)) for the requested rows (Y = X unless given)."""
     xt = np.asarray(xt, dtype=np.float64)
     xs = np.asarray(xs, dtype=np.float64)
+    yt = xt if yt is None else np.asarray(yt, dtype=np.float64)
+    ys = xs if ys is None else np.asarray(ys, dtype=np.float64)
     rows = np.asarray(list(rows), dtype=np.int64)
-    n = xt.shape[0]
+    n = yt.shape[0]
     keep = (np.arange(n)[None, :] <= rows[:, None]) if causal else np.ones((len(rows), n), bool)
-    zt = np.where(keep, scale * (xt[rows] @ xt.T), _NEG_INF)
-    zs = np.where(keep, scale * (xs[rows] @ xs.T), _NEG_INF)
+    zt = np.where(keep, scale * (xt[rows] @ yt.T), _NEG_INF)
+    zs = np.where(keep, scale * (xs[rows] @ ys.T), _NEG_INF)
     logr_t = np.where(keep, zt - _logsumexp_rows(zt)[:, None], 0.0)
     logr_s = np.where(keep, zs - _logsumexp_rows(zs)[:, None], 0.0)
     r_t = np.where(keep, np.exp(logr_t), 0.0)
@@ -187,6 +216,42 @@ def dx_rows(xt: np.ndarray, xs: np.ndarray, scale: float, rows: Iterable[int],
     cs = np.where(keep_c, np.exp(np.where(keep_c, scale * (xs[rows] @ xs.T) - lse_s[None, :], 0.0)), 0.0)
     col_term = ((cs - ct) / n) @ xs
     return scale * (row_term + col_term)
+
+
+def dx_rows_xy(xt: np.ndarray, xs: np.ndarray, yt: np.ndarray, ys: np.ndarray, scale: float,
+               rows: Iterable[int], lse_t: np.ndarray, lse_s: np.ndarray,
+               causal: bool = True) -> np.ndarray:
+    """Rows of dX_s = scale * dZ Y_s of an X/Y relation: sum_j dZ(i,j) y_s[j].
+
+    `lse_t`/`lse_s`: the oracle's LSE of the requested rows (or of all rows).
+    """
+    xt, xs, yt, ys = (np.asarray(v, dtype=np.float64) for v in (xt, xs, yt, ys))
+    rows = np.asarray(list(rows), dtype=np.int64)
+    n = yt.shape[0]
+    lt = np.asarray(lse_t)[rows] if len(lse_t) == n else np.asarray(lse_t)
+    ls = np.asarray(lse_s)[rows] if len(lse_s) == n else np.asarray(lse_s)
+    keep = (np.arange(n)[None, :] <= rows[:, None]) if causal else np.ones((len(rows), n), bool)
+    rt = np.where(keep, np.exp(np.where(keep, scale * (xt[rows] @ yt.T) - lt[:, None], 0.0)), 0.0)
+    rs = np.where(keep, np.exp(np.where(keep, scale * (xs[rows] @ ys.T) - ls[:, None], 0.0)), 0.0)
+    return scale * (((rs - rt) / n) @ ys)
+
+
+def dy_rows_xy(xt: np.ndarray, xs: np.ndarray, yt: np.ndarray, ys: np.ndarray, scale: float,
+               cols: Iterable[int], lse_t: np.ndarray, lse_s: np.ndarray,
+               causal: bool = True) -> np.ndarray:
+    """Rows j of dY_s = scale * dZ^T X_s of an X/Y relation: sum_i dZ(i,j) x_s[i].
+
+    Column j of dZ involves every row i (i >= j when causal), so `lse_t`/`lse_s`
+    are the oracle's LSE over ALL rows (from `lse_rows`).
+    """
+    xt, xs, yt, ys = (np.asarray(v, dtype=np.float64) for v in (xt, xs, yt, ys))
+    cols = np.asarray(list(cols), dtype=np.int64)
+    n = xt.shape[0]
+    keep = (np.arange(n)[None, :] >= cols[:, None]) if causal else np.ones((len(cols), n), bool)
+    # entries (i, j) of Z for the requested j, laid out as [j, i]
+    ct = np.where(keep, np.exp(np.where(keep, scale * (yt[cols] @ xt.T) - np.asarray(lse_t)[None, :], 0.0)), 0.0)
+    cs = np.where(keep, np.exp(np.where(keep, scale * (ys[cols] @ xs.T) - np.asarray(lse_s)[None, :], 0.0)), 0.0)
+    return scale * (((cs - ct) / n) @ xs)
 
 
 def forward_only_loss(xt: np.ndarray, xs: np.ndarray, scale: float,

@@ -139,3 +139,38 @@ def test_loss_workspace_checks(lib):
     assert _loss(lib, ws=FAKE + 16) == 3          # not 256-byte aligned
     assert _loss(lib, loss=None) == 1
     assert _loss(lib, xt=None) == 1
+
+
+def _xy(lib, fn, **kw):
+    a = dict(xt=FAKE, xs=FAKE, yt=FAKE, ys=FAKE, dt=0, B=1, H=2, n=64, d=128, scale=0.1, causal=1,
+             lt=FAKE, ls=FAKE, rk=FAKE, lscale=1.0, dx=FAKE, dy=FAKE, ws=FAKE, wsb=1 << 30, loss=FAKE)
+    a.update(kw)
+    head = (a["xt"], a["xs"], a["yt"], a["ys"], a["dt"], a["B"], a["H"], a["n"], a["d"], a["scale"], a["causal"])
+    if fn == "lse":
+        return lib.larard_xy_lse_fwd(*head, a["lt"], a["ls"], None)
+    if fn == "fwd":
+        return lib.larard_xy_kl_fwd(*head, a["lt"], a["ls"], a["rk"], None)
+    if fn == "bwd":
+        return lib.larard_xy_kl_bwd(*head, a["lt"], a["ls"], a["lscale"], a["rk"], a["dx"], a["dy"], None)
+    return lib.larard_xy_loss(*head, a["lscale"], a["ws"], a["wsb"], a["loss"], a["dx"], a["dy"], None)
+
+
+@pytest.mark.parametrize("fn", ["lse", "fwd", "bwd", "loss"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(yt=None), 1), (dict(ys=None), 1), (dict(yt=FAKE + 8), 1), (dict(xt=None), 1),
+    (dict(d=96), 2), (dict(dt=5), 2), (dict(scale=-1.0), 1),
+])
+def test_xy_validation(lib, fn, kw, code):
+    assert _xy(lib, fn, **kw) == code
+    assert lib.larard_last_error().decode() != ""
+
+
+def test_xy_specific_checks(lib):
+    assert _xy(lib, "bwd", rk=None) == 1
+    assert _xy(lib, "bwd", dy=FAKE + 4) == 1
+    assert _xy(lib, "fwd", rk=None) == 1
+    assert _xy(lib, "loss", ws=None) == 3
+    assert _xy(lib, "loss", dx=FAKE + 8) == 1
+    # n == 0 launches nothing and needs no pointer but the loss scalar of *_loss
+    for fn in ("lse", "fwd", "bwd"):
+        assert _xy(lib, fn, n=0, xt=None, xs=None, yt=None, ys=None, lt=None, ls=None, rk=None) == 0

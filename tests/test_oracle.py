@@ -208,3 +208,61 @@ def test_row_sampled_forms_match_dense(causal):
     assert np.max(np.abs(oracle.row_kl_rows(xt, xs, s, rows, causal) - r["row_kl"][rows])) < 1e-14
     got = oracle.dx_rows(xt, xs, s, rows, lt, ls, causal)
     assert np.max(np.abs(got - r["dself"][rows])) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# General relation X != Y (notes page, "Key designs" items 1 and 3).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("vals", [(0.3, 1.1, -0.4, 0.9, 0.7, -0.2, 1.3, 0.6, 0.8),
+                                  (1.5, -0.7, 1.2, 0.2, -0.9, 0.4, 0.1, 1.1, 0.35)])
+def test_cross_two_token_closed_form(vals):
+    # n=2, d=1, causal.  Row 1 has logits [s x1 y0, s x1 y1], so
+    # r(1,1) = sigmoid(s x1 (y1 - y0)); row 0 is the single entry (0,0).
+    x0t, x1t, x0s, x1s, y0t, y1t, y0s, y1s, s = vals
+    sig = lambda u: 1.0 / (1.0 + math.exp(-u))
+    p = sig(s * x1t * (y1t - y0t))
+    q = sig(s * x1s * (y1s - y0s))
+    kl1 = p * math.log(p / q) + (1 - p) * math.log((1 - p) / (1 - q))
+    r = oracle.relation_kl_head(np.array([[x0t], [x1t]]), np.array([[x0s], [x1s]]), s, True,
+                                np.array([[y0t], [y1t]]), np.array([[y0s], [y1s]]))
+    assert r["loss"] == pytest.approx(kl1 / 2, rel=1e-13, abs=1e-16)
+    # dZ(1,1) = (q - p)/2, dZ(1,0) = (p - q)/2, dZ(0,0) = 0
+    assert r["dxs"][0, 0] == pytest.approx(0.0, abs=1e-16)
+    assert r["dxs"][1, 0] == pytest.approx(s * (q - p) / 2 * (y1s - y0s), rel=1e-12, abs=1e-16)
+    assert r["dys"][0, 0] == pytest.approx(s * (p - q) / 2 * x1s, rel=1e-12, abs=1e-16)
+    assert r["dys"][1, 0] == pytest.approx(s * (q - p) / 2 * x1s, rel=1e-12, abs=1e-16)
+
+
+def test_cross_with_y_equal_x_is_the_self_relation():
+    rng = np.random.default_rng(31)
+    xt = rng.standard_normal((2, 2, 13, 5)); xs = xt + 0.3 * rng.standard_normal(xt.shape)
+    a = oracle.relation_kl_xy(xt, xs, xt, xs, 0.6, True, loss_scale=0.5)
+    b = oracle.relation_kl(xt, xs, 0.6, True, loss_scale=0.5)
+    assert a["loss"] == pytest.approx(b["loss"], rel=1e-14)
+    assert np.max(np.abs(a["dxs"] + a["dys"] - b["dxs"])) < 1e-15
+    assert np.array_equal(a["row_kl"], b["row_kl"])
+
+
+def test_cross_kl_nonnegative_and_zero_for_identical_models():
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((1, 2, 20, 6)); y = rng.standard_normal((1, 2, 20, 6))
+    r = oracle.relation_kl_xy(x, x + 0.5 * rng.standard_normal(x.shape), y, y, 0.5, True)
+    assert np.all(r["row_kl"] > -1e-15)
+    z = oracle.relation_kl_xy(x, x, y, y, 0.5, False)
+    assert z["loss"] == 0.0 and np.all(z["dxs"] == 0.0) and np.all(z["dys"] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_cross_row_sampled_forms_match_dense(causal):
+    rng = np.random.default_rng(33)
+    n, d, s = 40, 6, 0.45
+    xt = rng.standard_normal((n, d)); xs = xt + 0.4 * rng.standard_normal((n, d))
+    yt = rng.standard_normal((n, d)); ys = yt + 0.4 * rng.standard_normal((n, d))
+    r = oracle.relation_kl_head(xt, xs, s, causal, yt, ys)
+    rows = [0, 1, 19, 39]
+    lt = oracle.lse_rows(xt, s, range(n), causal, y=yt)
+    ls = oracle.lse_rows(xs, s, range(n), causal, y=ys)
+    assert np.max(np.abs(lt - r["lse_t"])) < 1e-13
+    assert np.max(np.abs(oracle.row_kl_rows(xt, xs, s, rows, causal, yt, ys) - r["row_kl"][rows])) < 1e-14
+    assert np.max(np.abs(oracle.dx_rows_xy(xt, xs, yt, ys, s, rows, lt, ls, causal) - r["dxs"][rows])) < 1e-15
+    assert np.max(np.abs(oracle.dy_rows_xy(xt, xs, yt, ys, s, rows, lt, ls, causal) - r["dys"][rows])) < 1e-15

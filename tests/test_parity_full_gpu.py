@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth_inputs as si
-from helpers import to_device
+from helpers import normwise_max_rel, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -100,3 +100,52 @@ def test_full_size_sampled(gpu_lib, name):
         assert np.max(np.abs(f_kl[b0, h0].cpu().numpy()[rows0] - oracle.row_kl_rows(a64, b64, s, rows0))) < kl_bound
         del xt, xs, dx, ws, f_lt, f_ls, f_kl
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["llama2_4k", "llama2_16k", "llama2_32k"])
+def test_full_size_query_key_relation(gpu_lib, name):
+    """X = Q, Y = K of the workload through larard_xy_loss; sampled rows and columns."""
+    import torch
+    w = si.WORKLOADS[name]
+    s = float(np.float32(w.scale))
+    maps = si.make_inputs(w, maps=["Q", "K"])
+    q, k = maps["Q"], maps["K"]
+    B, H, n, d = q.xt.shape
+    rng = np.random.default_rng(200 + w.seed)
+    print(f"\n[{name}] Q/K relation B={B} H={H} n={n} d={d}", flush=True)
+    xt, xs = to_device(q.xt, w.dtype), to_device(q.xs, w.dtype)
+    yt, ys = to_device(k.xt, w.dtype), to_device(k.xs, w.dtype)
+    ws = torch.empty(gpu_lib.workspace_bytes(B, H, n), dtype=torch.uint8, device="cuda")
+    loss, dx, dy = gpu_lib.xy_loss(xt, xs, yt, ys, w.scale, True, workspace=ws)
+    torch.cuda.synchronize()
+    off = gpu_lib.workspace_layout(B, H, n)
+    lse_t = ws[off[0]:off[0] + 8 * B * H * n].view(torch.float64).view(B, H, n)
+    lse_s = ws[off[1]:off[1] + 8 * B * H * n].view(torch.float64).view(B, H, n)
+    row_kl = ws[off[2]:off[2] + 4 * B * H * n].view(torch.float32).view(B, H, n)
+    assert bool(torch.isfinite(dx).all()) and bool(torch.isfinite(dy).all())
+    assert float(row_kl.min()) > -1e-5
+    want = float(row_kl.double().sum() / n)
+    assert abs(float(loss.cpu()) - want) <= 1e-6 * abs(want)
+    b, h = int(rng.integers(B)), int(rng.integers(H))
+    rows = _rows(n, rng)
+    a_t, a_s = q.head64(b, h)
+    c_t, c_s = k.head64(b, h)
+    lt = np.concatenate([oracle.lse_rows(a_t, s, range(r, min(r + 1024, n)), True, y=c_t) for r in range(0, n, 1024)])
+    ls = np.concatenate([oracle.lse_rows(a_s, s, range(r, min(r + 1024, n)), True, y=c_s) for r in range(0, n, 1024)])
+    kl = oracle.row_kl_rows(a_t, a_s, s, rows, True, c_t, c_s)
+    dxr = oracle.dx_rows_xy(a_t, a_s, c_t, c_s, s, rows, lt, ls, True)
+    dyr = oracle.dy_rows_xy(a_t, a_s, c_t, c_s, s, rows, lt, ls, True)
+    nx = max(np.max(np.linalg.norm(a_t, axis=1)), np.max(np.linalg.norm(a_s, axis=1)))
+    ny = max(np.max(np.linalg.norm(c_t, axis=1)), np.max(np.linalg.norm(c_s, axis=1)))
+    zmax = s * nx * ny
+    e_lse = max(np.max(np.abs(lse_t[b, h].cpu().numpy() - lt)), np.max(np.abs(lse_s[b, h].cpu().numpy() - ls)))
+    e_kl = np.max(np.abs(row_kl[b, h].cpu().numpy()[rows] - kl))
+    e_dx = normwise_max_rel(dx[b, h].cpu().numpy()[rows], dxr)
+    e_dy = normwise_max_rel(dy[b, h].cpu().numpy()[rows], dyr)
+    print(f"  head ({b},{h}): lse_err={e_lse:.2e} kl_err={e_kl:.2e} dx_maxrel={e_dx:.2e} dy_maxrel={e_dy:.2e}",
+          flush=True)
+    assert e_lse < 2e-6 * (1 + np.max(np.abs(lt))) + 8 * EPS32 * zmax
+    assert e_kl < 2e-6 + 1e-4 * np.max(np.abs(kl)) + 8 * EPS32 * zmax
+    assert e_dx < 2e-2 and e_dy < 2e-2
+    del xt, xs, yt, ys, dx, dy, ws
+    torch.cuda.empty_cache()
