@@ -313,6 +313,10 @@ def main():
     ms_step_oneshot = s2.elapsed_time(e2) / args.steps
     losses = {b["name"]: float(b["loss"].cpu()) for b in bufs}
 
+    def units(b):
+        return b["B"] * b["H"] * 2 * b["d"] * causal_pairs(b["n"])
+    step_flops = sum(6 * units(b) for b in bufs)
+
     # Forward-only loss (one phase-1 sweep with the KL accumulator + reduce),
     # timed the same way: 2 GEMM-units per head-map.
     def fwd_step():
@@ -330,6 +334,27 @@ def main():
     torch.cuda.synchronize()
     ms_fwd = s3.elapsed_time(e3) / args.steps
     losses_fwd = {b["name"]: float(b["loss"].cpu()) for b in bufs}
+
+    # The same step with every map in one launch per phase (larard_multi_loss).
+    wsm = torch.empty(lmr.multi_workspace_bytes([(b["xt"], b["xs"], 1.0, b["dx"]) for b in bufs]),
+                      dtype=torch.uint8, device=dev)
+    mlist = [(b["xt"], b["xs"], 1.0, b["dx"]) for b in bufs]
+    mloss = torch.empty((), dtype=torch.float32, device=dev)
+
+    def fused_step():
+        lmr.multi_loss(mlist, scale, True, 1.0, workspace=wsm, out=mloss)
+    for _ in range(args.warmup):
+        fused_step()
+    torch.cuda.synchronize()
+    s5, e5 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s5.record()
+    for _ in range(args.steps):
+        fused_step()
+    e5.record()
+    torch.cuda.synchronize()
+    ms_fused = s5.elapsed_time(e5) / args.steps
+    loss_fused = float(mloss.cpu())
+    del wsm
 
     # General relation X != Y on the same data: the query/key map (X = Q,
     # Y = K), fwd+bwd through one larard_xy_loss call (dX_s and dY_s).
@@ -367,9 +392,6 @@ def main():
     # carries phase 2's recompute (2) and the row term (1); the column sweep's
     # algorithmic share is the column term (1) -- its recompute is split-mode
     # overhead and is not counted.
-    def units(b):
-        return b["B"] * b["H"] * 2 * b["d"] * causal_pairs(b["n"])
-    step_flops = sum(6 * units(b) for b in bufs)
     alg = {"lse_fwd": 2, "kl_rows": 3, "kl_cols": 1, "reduce": 0}
     exe = {"lse_fwd": 2, "kl_rows": 3, "kl_cols": 3, "reduce": 0}
     kern = {}
@@ -422,6 +444,10 @@ def main():
                          "losses": losses_fwd,
                          "what": "larard_kl_fwd + reduce per map; algorithmic flops 2 GEMM-units per head-map"},
         "cross_relation": cross,
+        "fused_maps": {"ms_per_step": round(ms_fused, 4),
+                       "tflops": round(step_flops / (ms_fused * 1e-3) / 1e12, 3),
+                       "loss_sum": loss_fused,
+                       "what": "all maps in one launch per phase (larard_multi_loss, weights 1)"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, maps, args.cpu_sample_n)

@@ -197,6 +197,41 @@ larard_status larard_xy_loss(const void* x_t, const void* x_s, const void* y_t, 
                              void* workspace, size_t workspace_bytes,
                              float* loss, float* dx_s, float* dy_s, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Several self-relation maps in one launch per phase (notes page, "Key
+ * designs" item 1 and "Loss function / training strategy": the loss is the
+ * weighted sum of the Q/Q, K/K and V/V map losses, weights lambda = 1 in the
+ * pages).  Maps share B, n, d, dtype, scale and causal; each has its own head
+ * count (GQA: 32 query heads, 8 key/value heads) and weight.  Every kernel
+ * runs once over the heads of all maps, longest row blocks of every map
+ * first, so small maps fill the tail of large ones.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* x_t;   /* [B, H, n, d] teacher projections of this map (device) */
+  const void* x_s;   /* [B, H, n, d] student projections */
+  int64_t H;         /* heads of this map */
+  float weight;      /* lambda_m: multiplies this map's loss and gradient */
+  float* dx_s;       /* [B, H, n, d] fp32 gradient (OVERWRITTEN) or NULL */
+} larard_map;
+
+#define LARARD_MAX_MAPS 8
+
+/* Workspace of larard_multi_loss: larard_workspace_bytes(dtype, 1, B * sum_m H_m, n),
+ * laid out as larard_workspace_layout of that shape with map m's heads
+ * following those of maps 0..m-1.  Returns 0 for invalid arguments. */
+size_t larard_multi_workspace_bytes(larard_dtype dtype, int64_t B, int64_t n, const larard_map* maps,
+                                    int n_maps);
+
+/* *loss = loss_scale * sum_m weight_m * sum_{b,h} (1/n) sum_i KL_i(map m), and
+ * for each map dx_s = loss_scale * weight_m * scale * (dZ X_s + dZ^T X_s).
+ * Either every map has dx_s or none has (loss only: one sweep per map set).
+ * 1 <= n_maps <= LARARD_MAX_MAPS.  fp32 inputs run the precision kernels map
+ * by map. */
+larard_status larard_multi_loss(const larard_map* maps, int n_maps, larard_dtype dtype,
+                                int64_t B, int64_t n, int64_t d, float scale, int causal,
+                                float loss_scale, void* workspace, size_t workspace_bytes,
+                                float* loss, void* stream);
+
 /* Byte offsets of the regions larard_loss carves from its workspace:
  * off[0] = lse_t, off[1] = lse_s, off[2] = row_kl, off[3] = fp64 partials.
  * Returns LARARD_E_INVALID for invalid sizes. */

@@ -68,6 +68,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.larard_xy_loss.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, f32, i32, f32, vp, ctypes.c_size_t,
                                    vp, vp, vp, vp]
     lib.larard_xy_loss.restype = i32
+    lib.larard_multi_workspace_bytes.argtypes = [i32, i64, i64, ctypes.POINTER(LarardMap), i32]
+    lib.larard_multi_workspace_bytes.restype = ctypes.c_size_t
+    lib.larard_multi_loss.argtypes = [ctypes.POINTER(LarardMap), i32, i32, i64, i64, i64, f32, i32, f32, vp,
+                                      ctypes.c_size_t, vp, vp]
+    lib.larard_multi_loss.restype = i32
     lib.larard_status_str.argtypes = [i32]
     lib.larard_status_str.restype = ctypes.c_char_p
     lib.larard_last_error.argtypes = []
@@ -76,6 +81,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.larard_version.restype = ctypes.c_char_p
     _lib = lib
     return lib
+
+
+class LarardMap(ctypes.Structure):
+    """larard_map of larard.h: one self-relation map of a multi-map launch."""
+    _fields_ = [("x_t", ctypes.c_void_p), ("x_s", ctypes.c_void_p), ("H", ctypes.c_int64),
+                ("weight", ctypes.c_float), ("dx_s", ctypes.c_void_p)]
 
 
 def _check(status: int, where: str) -> None:
@@ -302,6 +313,51 @@ def xy_loss(xt, xs, yt, ys, scale=None, causal=True, loss_scale=1.0, need_grad=T
                                _stream())
     _check(st, "larard_xy_loss")
     return out, dx, dy
+
+
+# ---------------------------------------------------------------------------
+# Several self-relation maps (e.g. Q/Q, K/K, V/V with GQA head counts) in one
+# launch per phase.
+# ---------------------------------------------------------------------------
+def _map_array(maps):
+    arr = (LarardMap * len(maps))()
+    for k, (xt, xs, weight, dx) in enumerate(maps):
+        arr[k] = LarardMap(_ptr(xt), _ptr(xs), int(xt.shape[1]), float(weight), _ptr(dx))
+    return arr
+
+
+def multi_workspace_bytes(maps, dtype: int = BF16) -> int:
+    """maps: list of (x_t, x_s, weight, dx or None) with x [B, H_m, n, d]."""
+    B, _, n, _ = (int(v) for v in maps[0][0].shape)
+    return int(load().larard_multi_workspace_bytes(dtype, B, n, _map_array(maps), len(maps)))
+
+
+def multi_loss(maps, scale: Optional[float] = None, causal: bool = True, loss_scale: float = 1.0,
+               workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Weighted loss over several maps in one launch per phase.
+
+    maps: list of (x_t, x_s, weight, dx) -- dx an fp32 [B, H_m, n, d] tensor that
+    receives that map's gradient, or None for every map (loss only).
+    Returns the loss as a 0-d fp32 device tensor.
+    """
+    xt0 = maps[0][0]
+    B, _, n, d = (int(v) for v in xt0.shape)
+    for xt, xs, _, dx in maps:
+        _shape(xt, xs)
+        if xt.shape[0] != B or xt.shape[2] != n or xt.shape[3] != d or xt.dtype != xt0.dtype:
+            raise ValueError("maps must share B, n, d and dtype")
+    scale = default_scale(d) if scale is None else float(scale)
+    arr = _map_array(maps)
+    code = _dtype_code(xt0)
+    nbytes = int(load().larard_multi_workspace_bytes(code, B, n, arr, len(maps)))
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=xt0.device)
+    out = torch.empty((), dtype=torch.float32, device=xt0.device) if out is None else out
+    st = load().larard_multi_loss(arr, len(maps), code, B, n, d, scale, int(causal), float(loss_scale),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+                                  _stream())
+    _check(st, "larard_multi_loss")
+    return out
 
 
 def version() -> str:

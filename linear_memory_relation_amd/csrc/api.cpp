@@ -389,6 +389,109 @@ larard_status larard_xy_loss(const void* x_t, const void* x_s, const void* y_t, 
   return LARARD_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Several maps in one launch per phase (larard.h, larard_multi_loss).
+// ---------------------------------------------------------------------------
+static_assert(LARARD_MAX_MAPS == lmr::kMaxMaps, "map-set capacity");
+
+size_t larard_multi_workspace_bytes(larard_dtype dtype, int64_t B, int64_t n, const larard_map* maps, int n_maps) {
+  if (maps == nullptr || n_maps < 1 || n_maps > LARARD_MAX_MAPS || B < 1) return 0;
+  int64_t heads = 0;
+  for (int m = 0; m < n_maps; ++m) {
+    if (maps[m].H < 1 || maps[m].H > kMaxGrid) return 0;
+    heads += maps[m].H;
+  }
+  if (heads > kMaxGrid / B) return 0;
+  return larard_workspace_bytes(dtype, 1, B * heads, n);
+}
+
+larard_status larard_multi_loss(const larard_map* maps, int n_maps, larard_dtype dtype, int64_t B, int64_t n,
+                                int64_t d, float scale, int causal, float loss_scale, void* workspace,
+                                size_t workspace_bytes, float* loss, void* stream) {
+  if (maps == nullptr || n_maps < 1 || n_maps > LARARD_MAX_MAPS)
+    return fail(LARARD_E_INVALID, "n_maps must be in [1, %d] with a non-NULL map array", LARARD_MAX_MAPS);
+  int64_t heads = 0;
+  int with_dx = 0;
+  larard_status s;
+  for (int m = 0; m < n_maps; ++m) {
+    const larard_map& mp = maps[m];
+    if ((s = check_common(mp.x_t, mp.x_s, dtype, B, mp.H, n, d, scale)) != LARARD_OK) return s;
+    if (!std::isfinite(mp.weight)) return fail(LARARD_E_INVALID, "map %d: weight must be finite", m);
+    if (mp.dx_s != nullptr && !aligned(mp.dx_s, 16)) return fail(LARARD_E_INVALID, "map %d: dx_s must be 16-byte aligned", m);
+    with_dx += mp.dx_s != nullptr;
+    heads += mp.H;
+  }
+  if (with_dx != 0 && with_dx != n_maps) return fail(LARARD_E_INVALID, "either every map has dx_s or none has");
+  if (heads > kMaxGrid / B) return fail(LARARD_E_INVALID, "B * sum of heads too large");
+  const int64_t bh_all = B * heads;
+  const int64_t nblk = (n + kOwnRows - 1) / kOwnRows;
+  if (nblk > 0 && bh_all > kMaxGrid / nblk) return fail(LARARD_E_INVALID, "B*sum(H)*ceil(n/128) exceeds the launch grid");
+  if (!std::isfinite(loss_scale)) return fail(LARARD_E_INVALID, "loss_scale must be finite");
+  if (loss == nullptr || !aligned(loss, 4)) return fail(LARARD_E_INVALID, "loss must be a 4-byte aligned device pointer");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n == 0) {
+    const hipError_t e = lmr::launch_zero_scalar(loss, st);
+    return e == hipSuccess ? LARARD_OK : hip_fail(e, "zero loss launch");
+  }
+  size_t off[4];
+  if ((s = larard_workspace_layout(dtype, 1, bh_all, n, off)) != LARARD_OK) return s;
+  const size_t need = larard_workspace_bytes(dtype, 1, bh_all, n);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(LARARD_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(LARARD_E_WORKSPACE, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  double* lse_t = reinterpret_cast<double*>(ws + off[0]);
+  double* lse_s = reinterpret_cast<double*>(ws + off[1]);
+  float* row_kl = reinterpret_cast<float*>(ws + off[2]);
+  double* partials = reinterpret_cast<double*>(ws + off[3]);
+
+  lmr::MapSet set{};
+  int64_t head0[LARARD_MAX_MAPS + 1];
+  float weight[LARARD_MAX_MAPS];
+  head0[0] = 0;
+  for (int m = 0; m < n_maps; ++m) {
+    const larard_map& mp = maps[m];
+    lmr::SweepArgs a = make_args(mp.x_t, mp.x_s, dtype, B, mp.H, n, d, scale, causal);
+    const int64_t rows0 = head0[m] * n;
+    a.lse_t = lse_t + rows0;
+    a.lse_s = lse_s + rows0;
+    a.row_kl = row_kl + rows0;
+    a.dx = mp.dx_s;
+    const double gsd = (double)loss_scale * (double)mp.weight * (double)scale / (double)n;
+    a.grad_scale = (float)gsd;
+    a.grad_scale_d = gsd;
+    set.map[m] = a;
+    head0[m + 1] = head0[m] + B * mp.H;
+    set.head0[m] = head0[m];
+    weight[m] = mp.weight;
+  }
+  set.head0[n_maps] = head0[n_maps];
+  set.nmaps = n_maps;
+  hipError_t e = hipSuccess;
+  if (dtype == LARARD_FP32) {
+    // Precision mode: the fp64 kernels, map by map.
+    for (int m = 0; m < n_maps && e == hipSuccess; ++m) {
+      const lmr::SweepArgs& a = set.map[m];
+      if (with_dx == 0) {
+        e = lmr::launch_kl_fwd(a, st);
+      } else {
+        e = lmr::launch_lse_fwd(a, st);
+        if (e == hipSuccess) e = lmr::launch_kl_row(a, st);
+        if (e == hipSuccess) e = lmr::launch_kl_col(a, st);
+      }
+    }
+    if (e != hipSuccess) return hip_fail(e, "multi-map launch");
+  } else if (with_dx == 0) {
+    if ((e = lmr::launch_kl_fwd_multi(set, st)) != hipSuccess) return hip_fail(e, "multi-map kl_fwd launch");
+  } else {
+    if ((e = lmr::launch_lse_fwd_multi(set, st)) != hipSuccess) return hip_fail(e, "multi-map lse_fwd launch");
+    if ((e = lmr::launch_kl_row_multi(set, st)) != hipSuccess) return hip_fail(e, "multi-map row sweep launch");
+    if ((e = lmr::launch_kl_col_multi(set, st)) != hipSuccess) return hip_fail(e, "multi-map column sweep launch");
+  }
+  e = lmr::launch_reduce_weighted(row_kl, head0, weight, n_maps, (int)n, loss_scale, partials, loss, st);
+  return e == hipSuccess ? LARARD_OK : hip_fail(e, "loss reduction launch");
+}
+
 const char* larard_status_str(larard_status status) {
   switch (status) {
     case LARARD_OK: return "LARARD_OK";

@@ -29,6 +29,16 @@ struct SweepArgs {
   double grad_scale_d;   // the same factor in fp64 (fp32-input path)
 };
 
+// Several relation maps of equal n, d and dtype in one launch (e.g. Q/Q,
+// K/K, V/V with their own head counts).  Heads are numbered across maps:
+// map m owns heads head0[m] .. head0[m+1]-1 of the launch.
+constexpr int kMaxMaps = 8;
+struct MapSet {
+  SweepArgs map[kMaxMaps];
+  int64_t head0[kMaxMaps + 1];
+  int nmaps;
+};
+
 hipError_t launch_lse_fwd(const SweepArgs& a, hipStream_t st);
 // Phase 1 with the KL accumulator: LSE_t, LSE_s and row_kl in one sweep.
 hipError_t launch_kl_fwd(const SweepArgs& a, hipStream_t st);
@@ -46,6 +56,17 @@ hipError_t launch_wide_kl_col(const SweepArgs& a, hipStream_t st);
 // in a fixed order (deterministic).  partials: [bh] fp64 scratch.
 hipError_t launch_reduce(const float* row_kl, int64_t bh, int n, float loss_scale,
                          double* partials, float* loss, hipStream_t st);
+// Fused bf16 launches over a map set (row_kl / lse of all maps contiguous,
+// map m at head offset head0[m]); every map must have the same kind of
+// gradient output (all or none).
+hipError_t launch_lse_fwd_multi(const MapSet& s, hipStream_t st);
+hipError_t launch_kl_fwd_multi(const MapSet& s, hipStream_t st);
+hipError_t launch_kl_row_multi(const MapSet& s, hipStream_t st);
+hipError_t launch_kl_col_multi(const MapSet& s, hipStream_t st);
+// Weighted reduction: loss = loss_scale/n * sum_m weight[m] * (sum over the
+// heads and rows of map m of row_kl).
+hipError_t launch_reduce_weighted(const float* row_kl, const int64_t* head0, const float* weight, int nmaps,
+                                  int n, float loss_scale, double* partials, float* loss, hipStream_t st);
 // *loss = 0 (used when n == 0).
 hipError_t launch_zero_scalar(float* loss, hipStream_t st);
 

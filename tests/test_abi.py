@@ -174,3 +174,44 @@ def test_xy_specific_checks(lib):
     # n == 0 launches nothing and needs no pointer but the loss scalar of *_loss
     for fn in ("lse", "fwd", "bwd"):
         assert _xy(lib, fn, n=0, xt=None, xs=None, yt=None, ys=None, lt=None, ls=None, rk=None) == 0
+
+
+def _maps(lib, Hs=(32, 8, 8), dx=FAKE, weights=None):
+    import linear_memory_relation_amd as lmr
+    arr = (lmr.LarardMap * len(Hs))()
+    for k, H in enumerate(Hs):
+        w = 1.0 if weights is None else weights[k]
+        arr[k] = lmr.LarardMap(FAKE, FAKE, H, w, dx if not isinstance(dx, list) else dx[k])
+    return arr
+
+
+def test_multi_workspace_is_the_single_layout_over_all_heads(lib):
+    import linear_memory_relation_amd as lmr
+    arr = _maps(lib)
+    got = lib.larard_multi_workspace_bytes(0, 2, 100, arr, 3)
+    assert got == lmr.workspace_bytes(1, 2 * 48, 100)
+    assert lib.larard_multi_workspace_bytes(0, 2, 100, arr, 0) == 0
+    assert lib.larard_multi_workspace_bytes(0, 2, 100, arr, 9) == 0
+    assert lib.larard_multi_workspace_bytes(0, 2, 100, _maps(lib, Hs=(4, 0)), 2) == 0
+
+
+def _multi(lib, arr, nm, **kw):
+    a = dict(dt=0, B=2, n=64, d=128, scale=0.1, causal=1, lscale=1.0, ws=FAKE, wsb=1 << 30, loss=FAKE)
+    a.update(kw)
+    return lib.larard_multi_loss(arr, nm, a["dt"], a["B"], a["n"], a["d"], a["scale"], a["causal"], a["lscale"],
+                                 a["ws"], a["wsb"], a["loss"], None)
+
+
+def test_multi_loss_validation(lib):
+    arr = _maps(lib)
+    assert _multi(lib, arr, 0) == 1
+    assert _multi(lib, arr, 9) == 1
+    assert _multi(lib, None, 3) == 1
+    assert _multi(lib, _maps(lib, dx=[FAKE, None, FAKE]), 3) == 1          # all or none
+    assert _multi(lib, _maps(lib, weights=[1.0, float("nan"), 1.0]), 3) == 1
+    assert _multi(lib, _maps(lib, dx=FAKE + 4), 3) == 1
+    assert _multi(lib, arr, 3, d=96) == 2
+    assert _multi(lib, arr, 3, loss=None) == 1
+    assert _multi(lib, arr, 3, wsb=1024) == 3
+    assert _multi(lib, arr, 3, ws=FAKE + 64) == 3
+    assert lib.larard_last_error().decode() != ""

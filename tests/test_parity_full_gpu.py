@@ -149,3 +149,24 @@ def test_full_size_query_key_relation(gpu_lib, name):
     assert e_dx < 2e-2 and e_dy < 2e-2
     del xt, xs, yt, ys, dx, dy, ws
     torch.cuda.empty_cache()
+
+
+def test_full_size_fused_gqa_maps(gpu_lib):
+    """The GQA workload (Q/Q over 32 heads, K/K and V/V over 8, B=2, n=8192) in
+    one launch per phase: loss equals the per-map sum, gradients bit for bit."""
+    import torch
+    w = si.WORKLOADS["llama3_gqa_8k"]
+    maps = si.make_inputs(w)
+    dev = {k: (to_device(m.xt, w.dtype), to_device(m.xs, w.dtype)) for k, m in maps.items()}
+    dxs = {k: torch.empty(a.shape, dtype=torch.float32, device="cuda") for k, (a, _) in dev.items()}
+    loss = gpu_lib.multi_loss([(a, b, 1.0, dxs[k]) for k, (a, b) in dev.items()], w.scale, True)
+    torch.cuda.synchronize()
+    total = 0.0
+    for k, (a, b) in dev.items():
+        l1, dx1 = gpu_lib.loss(a, b, w.scale, True)
+        torch.cuda.synchronize()
+        total += float(l1.cpu())
+        assert torch.equal(dx1, dxs[k]), k
+        del dx1
+    print(f"\n  fused GQA loss {float(loss.cpu()):.6f} vs per-map sum {total:.6f}", flush=True)
+    assert abs(float(loss.cpu()) - total) <= 1e-6 * abs(total)

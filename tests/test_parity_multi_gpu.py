@@ -1,0 +1,63 @@
+"""Several maps in one launch per phase (larard_multi_loss) against per-map calls and the oracle.
+
+The fused kernels run the same per-head arithmetic as the per-map launches,
+only scheduled together, so each map's gradient must match the per-map path
+bit for bit (weights are powers of two, so the gradient scale rounds the
+same way); the loss is the weighted sum, reduced in fp64.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as si
+from helpers import normwise_max_rel, rel, to_device, widen
+
+pytestmark = pytest.mark.gpu
+
+
+def _maps_gqa(B, n, d, Hs, seed, dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    out = []
+    for H in Hs:
+        xt = rng.standard_normal((B, H, n, d)) * rng.uniform(0.5, 1.5, (1, H, 1, 1))
+        xs = xt + 0.3 * rng.standard_normal(xt.shape)
+        rnd = si.round_bf16_bits if dtype == "bf16" else si.round_f32
+        out.append((rnd(xt), rnd(xs)))
+    return out
+
+
+@pytest.mark.parametrize("n,d,causal", [(200, 128, True), (129, 64, True), (150, 128, False), (1, 128, True)])
+def test_multi_matches_per_map_and_oracle(gpu_lib, n, d, causal):
+    import torch
+    Hs, weights = (4, 2, 2), (1.0, 0.5, 2.0)
+    host = _maps_gqa(2, n, d, Hs, seed=n + d)
+    dev = [(to_device(a, "bf16"), to_device(b, "bf16")) for a, b in host]
+    s = 1.0 / np.sqrt(d)
+    dxs = [torch.empty(a.shape, dtype=torch.float32, device="cuda") for a, _ in dev]
+    loss = gpu_lib.multi_loss([(a, b, w, g) for (a, b), w, g in zip(dev, weights, dxs)], s, causal, 0.25)
+    loss_only = gpu_lib.multi_loss([(a, b, w, None) for (a, b), w in zip(dev, weights)], s, causal, 0.25)
+    singles = [gpu_lib.loss(a, b, s, causal, 0.25 * w) for (a, b), w in zip(dev, weights)]
+    torch.cuda.synchronize()
+    want = sum(float(l.cpu()) for l, _ in singles)
+    assert rel(float(loss.cpu()), want) < 1e-6
+    assert rel(float(loss_only.cpu()), want) < 1e-5 or abs(float(loss_only.cpu()) - want) < 1e-7
+    for g, (_, dx1) in zip(dxs, singles):
+        assert torch.equal(g, dx1)
+    # and against the oracle
+    ref = sum(w * oracle.relation_kl(widen(a, "bf16"), widen(b, "bf16"), float(np.float32(s)), causal)["loss"]
+              for (a, b), w in zip(host, weights)) * 0.25
+    if abs(ref) > 1e-6:
+        assert rel(float(loss.cpu()), ref) < 1e-3
+
+
+def test_multi_fp32(gpu_lib):
+    import torch
+    host = _maps_gqa(1, 90, 64, (2, 1), seed=5, dtype="f32")
+    dev = [(to_device(a, "f32"), to_device(b, "f32")) for a, b in host]
+    dxs = [torch.empty(a.shape, dtype=torch.float32, device="cuda") for a, _ in dev]
+    loss = gpu_lib.multi_loss([(a, b, 1.0, g) for (a, b), g in zip(dev, dxs)], 0.125, True)
+    torch.cuda.synchronize()
+    refs = [oracle.relation_kl(a.astype(np.float64), b.astype(np.float64), 0.125, True) for a, b in host]
+    assert rel(float(loss.cpu()), sum(r["loss"] for r in refs)) < 1e-5
+    for g, r in zip(dxs, refs):
+        assert normwise_max_rel(g.cpu().numpy(), r["dxs"]) < 1e-5
