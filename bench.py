@@ -356,6 +356,40 @@ def main():
     loss_fused = float(mloss.cpu())
     del wsm
 
+    # Projection backward of the first map: dW = h^T R^T(dX_s) with synthetic
+    # bf16 hidden states of model width H*d and the student rotation (PI).
+    proj = None
+    bq0 = bufs[0]
+    dm = bq0["H"] * bq0["d"]
+    if dm % 128 == 0:
+        g = torch.Generator(device=dev)
+        g.manual_seed(1234)
+        hst = torch.randn((bq0["B"], bq0["n"], dm), generator=g, device=dev).to(torch.bfloat16)
+        pos = torch.arange(bq0["n"], dtype=torch.float64) / (w.factor if w.kind == "pi" else 1.0)
+        inv = (w.base * (w.factor ** (bq0["d"] / (bq0["d"] - 2)) if w.kind == "ntk" else w.base)) ** (
+            -2.0 * torch.arange(bq0["d"] // 2, dtype=torch.float64) / bq0["d"])
+        ang = torch.outer(pos, inv)
+        rc, rs = torch.cos(ang).float().to(dev), torch.sin(ang).float().to(dev)
+        wsp = torch.empty(int(lmr.load().larard_proj_bwd_workspace_bytes(bq0["B"], bq0["n"], dm, bq0["H"], bq0["d"])),
+                          dtype=torch.uint8, device=dev)
+        dW = torch.empty((dm, dm), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            lmr.proj_bwd(hst, bq0["dx"], rc, rs, workspace=wsp, out=dW)
+        torch.cuda.synchronize()
+        s6, e6 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s6.record()
+        for _ in range(args.steps):
+            lmr.proj_bwd(hst, bq0["dx"], rc, rs, workspace=wsp, out=dW)
+        e6.record()
+        torch.cuda.synchronize()
+        ms_p = s6.elapsed_time(e6) / args.steps
+        pflops = 2.0 * dm * dm * bq0["B"] * bq0["n"]
+        proj = {"ms": round(ms_p, 4), "tflops": round(pflops / (ms_p * 1e-3) / 1e12, 3),
+                "pct_bf16_peak": round(100 * pflops / (ms_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                "what": f"larard_proj_bwd for map {bq0['name']}: dW [{dm}x{dm}] = h^T R^T(dX_s), "
+                        f"K = B*n = {bq0['B'] * bq0['n']}; synthetic bf16 h; flops 2*dm*H*d*B*n"}
+        del hst, wsp, dW
+
     # General relation X != Y on the same data: the query/key map (X = Q,
     # Y = K), fwd+bwd through one larard_xy_loss call (dX_s and dY_s).
     cross = None
@@ -444,6 +478,7 @@ def main():
                          "losses": losses_fwd,
                          "what": "larard_kl_fwd + reduce per map; algorithmic flops 2 GEMM-units per head-map"},
         "cross_relation": cross,
+        "proj_bwd": proj,
         "fused_maps": {"ms_per_step": round(ms_fused, 4),
                        "tflops": round(step_flops / (ms_fused * 1e-3) / 1e12, 3),
                        "loss_sum": loss_fused,

@@ -232,6 +232,28 @@ larard_status larard_multi_loss(const larard_map* maps, int n_maps, larard_dtype
                                 float loss_scale, void* workspace, size_t workspace_bytes,
                                 float* loss, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Projection backward: the gradient of the student projection weights
+ * (notes page, "Method details -> Overall framework" and "Loss function /
+ * training strategy": stage 1 updates only W_q, W_k, W_v).  With hidden
+ * states h [B, n, dm] and per-head student projections
+ *     X_s[b,hd,i,:] = R(i) (h[b,i,:] W[:, hd*d:(hd+1)*d]),
+ * R(i) the student's rotate-half rotation at token i (pairs k, k + d/2,
+ * angle table entries cos/sin[i, k]) or the identity (V, tables NULL):
+ *     dw[c, hd*d + k] = sum_{b,i} h[b,i,c] (R(i)^T dX_s[b,hd,i,:])_k.
+ * h: bf16 [B, n, dm] device, 16-byte aligned; dx_s: fp32 [B, H, n, d] (e.g.
+ * the dx_s of larard_loss); rope_cos / rope_sin: fp32 [n, d/2] device or both
+ * NULL; dw: fp32 [dm, H*d], OVERWRITTEN.  R^T dX_s is rounded to bf16 and
+ * contracted on bf16 MFMA with fp32 accumulation.  dm and H*d must be
+ * multiples of 128 (LARARD_E_UNSUPPORTED otherwise), d 64 or 128.  The
+ * workspace (device, 256-byte aligned) holds the K-major bf16 operands.
+ * ------------------------------------------------------------------------- */
+size_t larard_proj_bwd_workspace_bytes(int64_t B, int64_t n, int64_t dm, int64_t H, int64_t d);
+
+larard_status larard_proj_bwd(const void* h, const float* dx_s, int64_t B, int64_t n, int64_t dm,
+                              int64_t H, int64_t d, const float* rope_cos, const float* rope_sin,
+                              void* workspace, size_t workspace_bytes, float* dw, void* stream);
+
 /* Byte offsets of the regions larard_loss carves from its workspace:
  * off[0] = lse_t, off[1] = lse_s, off[2] = row_kl, off[3] = fp64 partials.
  * Returns LARARD_E_INVALID for invalid sizes. */

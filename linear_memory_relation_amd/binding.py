@@ -73,6 +73,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.larard_multi_loss.argtypes = [ctypes.POINTER(LarardMap), i32, i32, i64, i64, i64, f32, i32, f32, vp,
                                       ctypes.c_size_t, vp, vp]
     lib.larard_multi_loss.restype = i32
+    lib.larard_proj_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.larard_proj_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.larard_proj_bwd.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.larard_proj_bwd.restype = i32
     lib.larard_status_str.argtypes = [i32]
     lib.larard_status_str.restype = ctypes.c_char_p
     lib.larard_last_error.argtypes = []
@@ -357,6 +361,31 @@ def multi_loss(maps, scale: Optional[float] = None, causal: bool = True, loss_sc
                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
                                   _stream())
     _check(st, "larard_multi_loss")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Projection backward: dW = h^T R^T(dX_s).
+# ---------------------------------------------------------------------------
+def proj_bwd(h: torch.Tensor, dx_s: torch.Tensor, rope_cos: Optional[torch.Tensor] = None,
+             rope_sin: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """h: bf16 [B, n, dm]; dx_s: fp32 [B, H, n, d]; rope tables fp32 [n, d/2] or None.
+    Returns dW fp32 [dm, H*d]."""
+    B, n, dm = (int(v) for v in h.shape)
+    _, H, n2, d = (int(v) for v in dx_s.shape)
+    if n2 != n or dx_s.shape[0] != B or h.dtype != torch.bfloat16 or dx_s.dtype != torch.float32:
+        raise ValueError("h must be bf16 [B, n, dm] and dx_s fp32 [B, H, n, d]")
+    if not (h.is_contiguous() and dx_s.is_contiguous()):
+        raise ValueError("h and dx_s must be contiguous")
+    nbytes = int(load().larard_proj_bwd_workspace_bytes(B, n, dm, H, d))
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=h.device)
+    out = torch.empty((dm, H * d), dtype=torch.float32, device=h.device) if out is None else out
+    st = load().larard_proj_bwd(_ptr(h), _ptr(dx_s), B, n, dm, H, d, _ptr(rope_cos), _ptr(rope_sin),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+                                _stream())
+    _check(st, "larard_proj_bwd")
     return out
 
 

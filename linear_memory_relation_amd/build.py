@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblarard.so")
 ARCH = "gfx950"
 
-SOURCES = ["kernels.hip", "wide.hip", "api.cpp"]
+SOURCES = ["kernels.hip", "wide.hip", "proj.hip", "api.cpp"]
 # Everything the library is built from; its hash is stamped into larard_version().
 STAMPED = [os.path.join(CSRC, f) for f in (*SOURCES, "launch.h")] + [os.path.join(INCLUDE, "larard.h")]
 

@@ -492,6 +492,63 @@ larard_status larard_multi_loss(const larard_map* maps, int n_maps, larard_dtype
   return e == hipSuccess ? LARARD_OK : hip_fail(e, "loss reduction launch");
 }
 
+// ---------------------------------------------------------------------------
+// Projection backward (larard.h, larard_proj_bwd).
+// ---------------------------------------------------------------------------
+namespace {
+bool proj_sizes_ok(int64_t B, int64_t n, int64_t dm, int64_t H, int64_t d) {
+  return B >= 1 && H >= 1 && n >= 0 && n <= kMaxN && (d == 64 || d == 128) && dm >= 128 && dm % 128 == 0 &&
+         (H * d) % 128 == 0 && dm / 64 <= 65535 && H <= 65535 && B <= kMaxGrid / (n > 0 ? n : 1);
+}
+int64_t proj_kp(int64_t B, int64_t n) { return (B * n + 63) / 64 * 64; }
+}  // namespace
+
+size_t larard_proj_bwd_workspace_bytes(int64_t B, int64_t n, int64_t dm, int64_t H, int64_t d) {
+  if (!proj_sizes_ok(B, n, dm, H, d)) return 0;
+  const size_t kp = (size_t)proj_kp(B, n);
+  return align256((size_t)(H * d) * kp * 2) + align256((size_t)dm * kp * 2);
+}
+
+larard_status larard_proj_bwd(const void* h, const float* dx_s, int64_t B, int64_t n, int64_t dm, int64_t H,
+                              int64_t d, const float* rope_cos, const float* rope_sin, void* workspace,
+                              size_t workspace_bytes, float* dw, void* stream) {
+  if (!proj_sizes_ok(B, n, dm, H, d)) {
+    if (d != 64 && d != 128) return fail(LARARD_E_UNSUPPORTED, "head dim d=%lld not supported (64 or 128)", (long long)d);
+    if (dm < 128 || dm % 128 != 0 || (H * d) % 128 != 0)
+      return fail(LARARD_E_UNSUPPORTED, "model dim and H*d must be multiples of 128 (got %lld, %lld)",
+                  (long long)dm, (long long)(H * d));
+    return fail(LARARD_E_INVALID, "invalid sizes B=%lld n=%lld dm=%lld H=%lld", (long long)B, (long long)n,
+                (long long)dm, (long long)H);
+  }
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(LARARD_E_INVALID, "rope_cos and rope_sin must both be given or both be NULL");
+  if (rope_cos != nullptr && (!aligned(rope_cos, 4) || !aligned(rope_sin, 4)))
+    return fail(LARARD_E_INVALID, "rope tables must be 4-byte aligned");
+  if (n > 0 && (h == nullptr || dx_s == nullptr || !aligned(h, 16) || !aligned(dx_s, 16)))
+    return fail(LARARD_E_INVALID, "h and dx_s must be 16-byte aligned device pointers");
+  if (dw == nullptr || !aligned(dw, 16)) return fail(LARARD_E_INVALID, "dw must be a 16-byte aligned device pointer");
+  const size_t need = larard_proj_bwd_workspace_bytes(B, n, dm, H, d);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(LARARD_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (need > 0 && !aligned(workspace, 256)) return fail(LARARD_E_WORKSPACE, "workspace must be 256-byte aligned");
+  lmr::ProjArgs p{};
+  p.h = static_cast<const uint16_t*>(h);
+  p.dx = dx_s;
+  p.cos = rope_cos;
+  p.sin = rope_sin;
+  p.B = B;
+  p.n = n;
+  p.dm = dm;
+  p.H = H;
+  p.d = d;
+  p.kp = proj_kp(B, n);
+  p.gt = static_cast<uint16_t*>(workspace);
+  p.ht = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + align256((size_t)(H * d) * (size_t)p.kp * 2));
+  p.dw = dw;
+  const hipError_t e = lmr::launch_proj_bwd(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LARARD_OK : hip_fail(e, "proj_bwd launch");
+}
+
 const char* larard_status_str(larard_status status) {
   switch (status) {
     case LARARD_OK: return "LARARD_OK";

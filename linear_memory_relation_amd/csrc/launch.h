@@ -67,6 +67,20 @@ hipError_t launch_kl_col_multi(const MapSet& s, hipStream_t st);
 // heads and rows of map m of row_kl).
 hipError_t launch_reduce_weighted(const float* row_kl, const int64_t* head0, const float* weight, int nmaps,
                                   int n, float loss_scale, double* partials, float* loss, hipStream_t st);
+// Projection backward (proj.hip): dW[dm, H*d] = h^T R^T(dX_s).
+struct ProjArgs {
+  const uint16_t* h;     // [B*n, dm] bf16 hidden states
+  const float* dx;       // [B, H, n, d] fp32 student gradient
+  const float* cos;      // [n, d/2] fp32 student rotation tables (null: no rotation)
+  const float* sin;
+  uint16_t* gt;          // workspace: G^T [H*d, kp] bf16
+  uint16_t* ht;          // workspace: h^T [dm, kp] bf16
+  float* dw;             // [dm, H*d] fp32 output
+  int64_t B, n, dm, H, d;
+  int64_t kp;            // B*n rounded up to a multiple of 64
+};
+hipError_t launch_proj_bwd(const ProjArgs& p, hipStream_t st);
+
 // *loss = 0 (used when n == 0).
 hipError_t launch_zero_scalar(float* loss, hipStream_t st);
 

@@ -254,6 +254,45 @@ def dy_rows_xy(xt: np.ndarray, xs: np.ndarray, yt: np.ndarray, ys: np.ndarray, s
     return scale * (((cs - ct) / n) @ xs)
 
 
+# ----------------------------------------------------------------------------
+# Projection backward (notes page, "Method details -> Overall framework" and
+# "Loss function / training strategy": stage 1 updates only the attention
+# projections).  X_s[b,h,i,:] = R(i) (h[b,i,:] W[:, h*d:(h+1)*d]) with R(i)
+# the student's rotate-half rotation, so dW = h^T (R^T dX_s).
+# ----------------------------------------------------------------------------
+
+def rope_rotate(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotate-half rotation of [..., n, d]: pair (k, k+d/2) turned by the angle
+    whose cos/sin are cos[i, k], sin[i, k] ([n, d/2] tables)."""
+    x = np.asarray(x, dtype=np.float64)
+    half = x.shape[-1] // 2
+    x1, x2 = x[..., :half], x[..., half:]
+    c, s = np.asarray(cos, np.float64), np.asarray(sin, np.float64)
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def rope_rotate_transpose(g: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """R(i)^T applied to [..., n, d] (the rotation by the opposite angle)."""
+    g = np.asarray(g, dtype=np.float64)
+    half = g.shape[-1] // 2
+    g1, g2 = g[..., :half], g[..., half:]
+    c, s = np.asarray(cos, np.float64), np.asarray(sin, np.float64)
+    return np.concatenate([g1 * c + g2 * s, g2 * c - g1 * s], axis=-1)
+
+
+def proj_bwd(h: np.ndarray, dxs: np.ndarray, cos: Optional[np.ndarray] = None,
+             sin: Optional[np.ndarray] = None) -> np.ndarray:
+    """dW [dm, H*d] = sum over (b, i) of h[b,i,:]^T (R(i)^T dX_s[b,:,i,:]) (heads side by side).
+
+    h: [B, n, dm]; dxs: [B, H, n, d]; cos/sin: [n, d/2] tables or None (no rotation).
+    """
+    h = np.asarray(h, dtype=np.float64)
+    g = np.asarray(dxs, dtype=np.float64) if cos is None else rope_rotate_transpose(dxs, cos, sin)
+    B, H, n, d = g.shape
+    gm = np.transpose(g, (0, 2, 1, 3)).reshape(B * n, H * d)
+    return h.reshape(B * n, h.shape[-1]).T @ gm
+
+
 def forward_only_loss(xt: np.ndarray, xs: np.ndarray, scale: float,
                       causal: bool = True) -> float:
     """Per-head loss only (row mean of KL), via the dense definition."""

@@ -215,3 +215,27 @@ def test_multi_loss_validation(lib):
     assert _multi(lib, arr, 3, wsb=1024) == 3
     assert _multi(lib, arr, 3, ws=FAKE + 64) == 3
     assert lib.larard_last_error().decode() != ""
+
+
+def _proj(lib, **kw):
+    a = dict(h=FAKE, dx=FAKE, B=1, n=100, dm=256, H=2, d=128, c=FAKE, s=FAKE, ws=FAKE, wsb=1 << 30, dw=FAKE)
+    a.update(kw)
+    return lib.larard_proj_bwd(a["h"], a["dx"], a["B"], a["n"], a["dm"], a["H"], a["d"], a["c"], a["s"], a["ws"],
+                               a["wsb"], a["dw"], None)
+
+
+def test_proj_bwd_workspace_and_validation(lib):
+    kp = (2 * 100 + 63) // 64 * 64
+    up = lambda v: (v + 255) // 256 * 256
+    assert lib.larard_proj_bwd_workspace_bytes(2, 100, 256, 2, 128) == up(256 * kp * 2) + up(256 * kp * 2)
+    assert lib.larard_proj_bwd_workspace_bytes(1, 100, 200, 2, 128) == 0       # dm not a multiple of 128
+    assert _proj(lib, dm=192) == 2
+    assert _proj(lib, H=1, d=64) == 2                                          # H*d = 64
+    assert _proj(lib, d=96) == 2
+    assert _proj(lib, c=None) == 1                                             # tables come in pairs
+    assert _proj(lib, h=None) == 1
+    assert _proj(lib, dx=FAKE + 4) == 1
+    assert _proj(lib, dw=None) == 1
+    assert _proj(lib, wsb=1024) == 3
+    assert _proj(lib, ws=FAKE + 16) == 3
+    assert _proj(lib, B=0) == 1

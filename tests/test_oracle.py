@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth_inputs as si
 
 RNG = np.random.default_rng(1234)
 
@@ -266,3 +267,66 @@ def test_cross_row_sampled_forms_match_dense(causal):
     assert np.max(np.abs(oracle.row_kl_rows(xt, xs, s, rows, causal, yt, ys) - r["row_kl"][rows])) < 1e-14
     assert np.max(np.abs(oracle.dx_rows_xy(xt, xs, yt, ys, s, rows, lt, ls, causal) - r["dxs"][rows])) < 1e-15
     assert np.max(np.abs(oracle.dy_rows_xy(xt, xs, yt, ys, s, rows, lt, ls, causal) - r["dys"][rows])) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# Projection backward (dW = h^T R^T dX_s).
+# ---------------------------------------------------------------------------
+def _tables(n, d, base=1.0e4, pos_scale=2.0):
+    c, s = si.rope_tables(n, d, base, pos_scale)
+    return c[:, : d // 2], s[:, : d // 2]
+
+
+def test_rope_rotation_transpose_and_generator_agree():
+    rng = np.random.default_rng(41)
+    n, d = 9, 8
+    c, s = _tables(n, d)
+    x = rng.standard_normal((2, 3, n, d))
+    y = oracle.rope_rotate(x, c, s)
+    assert np.max(np.abs(oracle.rope_rotate_transpose(y, c, s) - x)) < 1e-14      # R^T R = I
+    assert np.allclose(np.sum(y ** 2, -1), np.sum(x ** 2, -1), rtol=1e-14)         # a rotation
+    full_c, full_s = si.rope_tables(n, d, 1.0e4, 2.0)
+    assert np.max(np.abs(y - si.apply_rope(x, full_c, full_s))) < 1e-14             # input convention
+    # a unit pair at angle theta goes to (cos theta, sin theta)
+    e = np.zeros((1, 1, n, d)); e[..., 0] = 1.0
+    r = oracle.rope_rotate(e, c, s)
+    assert np.allclose(r[0, 0, :, 0], c[:, 0]) and np.allclose(r[0, 0, :, d // 2], s[:, 0])
+
+
+def test_proj_bwd_matches_finite_differences_through_rope_and_relation():
+    # L(W) = relation KL of teacher X_t and student X_s = R (h W), per head.
+    rng = np.random.default_rng(42)
+    B, n, dm, H, d, scale = 1, 7, 5, 2, 4, 0.6
+    c, s = _tables(n, d)
+    h = rng.standard_normal((B, n, dm))
+    W = rng.standard_normal((dm, H * d)) * 0.5
+    xt = rng.standard_normal((B, H, n, d))
+
+    def xs_of(Wm):
+        p = (h @ Wm).reshape(B, n, H, d).transpose(0, 2, 1, 3)
+        return oracle.rope_rotate(p, c, s)
+
+    def loss(Wm):
+        return oracle.relation_kl(xt, xs_of(Wm), scale, True)["loss"]
+
+    dxs = oracle.relation_kl(xt, xs_of(W), scale, True)["dxs"]
+    dW = oracle.proj_bwd(h, dxs, c, s)
+    eps = 1e-6
+    for (a, b) in [(0, 0), (1, 3), (4, 5), (2, 7), (3, 1)]:
+        Wp, Wn = W.copy(), W.copy()
+        Wp[a, b] += eps
+        Wn[a, b] -= eps
+        fd = (loss(Wp) - loss(Wn)) / (2 * eps)
+        assert abs(fd - dW[a, b]) < 1e-7 * max(1.0, abs(dW[a, b])), (a, b, fd, dW[a, b])
+
+
+def test_proj_bwd_without_rotation_is_a_plain_product():
+    rng = np.random.default_rng(43)
+    h = rng.standard_normal((2, 5, 3)); g = rng.standard_normal((2, 2, 5, 4))
+    got = oracle.proj_bwd(h, g)
+    want = np.zeros((3, 8))
+    for b in range(2):
+        for i in range(5):
+            for hd in range(2):
+                want[:, hd * 4:(hd + 1) * 4] += np.outer(h[b, i], g[b, hd, i])
+    assert np.max(np.abs(got - want)) < 1e-14

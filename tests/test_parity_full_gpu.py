@@ -170,3 +170,30 @@ def test_full_size_fused_gqa_maps(gpu_lib):
         del dx1
     print(f"\n  fused GQA loss {float(loss.cpu()):.6f} vs per-map sum {total:.6f}", flush=True)
     assert abs(float(loss.cpu()) - total) <= 1e-6 * abs(total)
+
+
+def test_full_size_proj_bwd():
+    """dW = h^T R^T(dX_s) at the 16K query shape (B=1, n=16384, dm=4096, H=32,
+    d=128, student PI x8 rotation), seeded synthetic h and dX_s, sampled rows."""
+    import torch
+    import linear_memory_relation_amd as lmr
+    lmr.load()
+    B, n, dm, H, d = 1, 16384, 4096, 32, 128
+    rng = np.random.default_rng(300)
+    h = si.round_bf16_bits(rng.standard_normal((B, n, dm), dtype=np.float32).astype(np.float64))
+    dx = si.round_f32(rng.standard_normal((B, H, n, d), dtype=np.float32).astype(np.float64) * 1e-4)
+    c, s = si.rope_tables(n, d, 1.0e4, 8.0)
+    c, s = si.round_f32(c[:, : d // 2]), si.round_f32(s[:, : d // 2])
+    dW = lmr.proj_bwd(to_device(h, "bf16"), torch.from_numpy(dx).cuda(), torch.from_numpy(c).cuda(),
+                      torch.from_numpy(s).cuda())
+    torch.cuda.synchronize()
+    rows = sorted(set([0, 1, 127, 128, 2047, 4095] + list(rng.choice(dm, 4, replace=False))))
+    got = dW[rows].cpu().numpy()
+    del dW
+    g = oracle.rope_rotate_transpose(dx.astype(np.float64), c, s)          # [B, H, n, d]
+    gm = np.transpose(g, (0, 2, 1, 3)).reshape(B * n, H * d)
+    hm = si.bf16_bits_to_f64(h.reshape(B * n, dm)[:, rows])
+    ref = hm.T @ gm
+    e = normwise_max_rel(got, ref)
+    print(f"\n  proj_bwd 16K sampled rows {rows}: normwise max-rel {e:.2e}", flush=True)
+    assert e < 1e-2
