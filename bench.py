@@ -45,6 +45,10 @@ def parse():
                    help="write the markdown summary of rocprofv3 kernel-trace/stats and FETCH_SIZE/WRITE_SIZE "
                         "runs of this script to stdout and exit")
     p.add_argument("--trace-cmd", default="", help="(with --summarize) command lines to record in the summary")
+    p.add_argument("--core-only", action="store_true",
+                   help="time only the step (and its one-call check): skip the forward-only, fused-map, "
+                        "projection and cross-relation sections, whose launches share kernel symbols with "
+                        "the step and would mix into a profiler's per-kernel averages")
     return p.parse_args()
 
 
@@ -201,6 +205,126 @@ def recorded_traffic(kind: str, workload: str):
     return val
 
 
+def extra_sections(args, bufs, w, scale, dev, units, step_flops):
+    """Timings beside the step: forward-only loss, all maps fused in one launch
+    per phase, the projection backward and the query/key cross relation."""
+    import torch
+    import linear_memory_relation_amd as lmr
+    # Forward-only loss (one phase-1 sweep with the KL accumulator + reduce),
+    # timed the same way: 2 GEMM-units per head-map.
+    def fwd_step():
+        for b in bufs:
+            lmr.kl_fwd(b["xt"], b["xs"], scale, True, b["lse_t"], b["lse_s"], b["row_kl"])
+            lmr.reduce_loss(b["row_kl"], b["partials"], b["loss"], 1.0)
+    for _ in range(args.warmup):
+        fwd_step()
+    torch.cuda.synchronize()
+    s3, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s3.record()
+    for _ in range(args.steps):
+        fwd_step()
+    e3.record()
+    torch.cuda.synchronize()
+    ms_fwd = s3.elapsed_time(e3) / args.steps
+    losses_fwd = {b["name"]: float(b["loss"].cpu()) for b in bufs}
+    fwd_info = {"ms_per_step": round(ms_fwd, 4),
+                "tflops": round(sum(2 * units(b) for b in bufs) / (ms_fwd * 1e-3) / 1e12, 3),
+                "pct_bf16_peak": round(100 * sum(2 * units(b) for b in bufs) / (ms_fwd * 1e-3) / 1e12
+                                       / PEAK_BF16_TFLOPS, 2),
+                "losses": losses_fwd,
+                "what": "larard_kl_fwd + reduce per map; algorithmic flops 2 GEMM-units per head-map"}
+
+    # The same step with every map in one launch per phase (larard_multi_loss).
+    wsm = torch.empty(lmr.multi_workspace_bytes([(b["xt"], b["xs"], 1.0, b["dx"]) for b in bufs]),
+                      dtype=torch.uint8, device=dev)
+    mlist = [(b["xt"], b["xs"], 1.0, b["dx"]) for b in bufs]
+    mloss = torch.empty((), dtype=torch.float32, device=dev)
+
+    def fused_step():
+        lmr.multi_loss(mlist, scale, True, 1.0, workspace=wsm, out=mloss)
+    for _ in range(args.warmup):
+        fused_step()
+    torch.cuda.synchronize()
+    s5, e5 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s5.record()
+    for _ in range(args.steps):
+        fused_step()
+    e5.record()
+    torch.cuda.synchronize()
+    ms_fused = s5.elapsed_time(e5) / args.steps
+    fused_info = {"ms_per_step": round(ms_fused, 4),
+                  "tflops": round(step_flops / (ms_fused * 1e-3) / 1e12, 3),
+                  "loss_sum": float(mloss.cpu()),
+                  "what": "all maps in one launch per phase (larard_multi_loss, weights 1)"}
+    del wsm
+
+    # Projection backward of the first map: dW = h^T R^T(dX_s) with synthetic
+    # bf16 hidden states of model width H*d and the student rotation (PI).
+    proj = None
+    bq0 = bufs[0]
+    dm = bq0["H"] * bq0["d"]
+    if dm % 128 == 0:
+        g = torch.Generator(device=dev)
+        g.manual_seed(1234)
+        hst = torch.randn((bq0["B"], bq0["n"], dm), generator=g, device=dev).to(torch.bfloat16)
+        pos = torch.arange(bq0["n"], dtype=torch.float64) / (w.factor if w.kind == "pi" else 1.0)
+        inv = (w.base * (w.factor ** (bq0["d"] / (bq0["d"] - 2)) if w.kind == "ntk" else w.base)) ** (
+            -2.0 * torch.arange(bq0["d"] // 2, dtype=torch.float64) / bq0["d"])
+        ang = torch.outer(pos, inv)
+        rc, rs = torch.cos(ang).float().to(dev), torch.sin(ang).float().to(dev)
+        wsp = torch.empty(int(lmr.load().larard_proj_bwd_workspace_bytes(bq0["B"], bq0["n"], dm, bq0["H"], bq0["d"])),
+                          dtype=torch.uint8, device=dev)
+        dW = torch.empty((dm, dm), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            lmr.proj_bwd(hst, bq0["dx"], rc, rs, workspace=wsp, out=dW)
+        torch.cuda.synchronize()
+        s6, e6 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s6.record()
+        for _ in range(args.steps):
+            lmr.proj_bwd(hst, bq0["dx"], rc, rs, workspace=wsp, out=dW)
+        e6.record()
+        torch.cuda.synchronize()
+        ms_p = s6.elapsed_time(e6) / args.steps
+        pflops = 2.0 * dm * dm * bq0["B"] * bq0["n"]
+        proj = {"ms": round(ms_p, 4), "tflops": round(pflops / (ms_p * 1e-3) / 1e12, 3),
+                "pct_bf16_peak": round(100 * pflops / (ms_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                "what": f"larard_proj_bwd for map {bq0['name']}: dW [{dm}x{dm}] = h^T R^T(dX_s), "
+                        f"K = B*n = {bq0['B'] * bq0['n']}; synthetic bf16 h; flops 2*dm*H*d*B*n"}
+        del hst, wsp, dW
+
+    # General relation X != Y on the same data: the query/key map (X = Q,
+    # Y = K), fwd+bwd through one larard_xy_loss call (dX_s and dY_s).
+    cross = None
+    names = [b["name"] for b in bufs]
+    if "Q" in names and "K" in names:
+        bq, bk = bufs[names.index("Q")], bufs[names.index("K")]
+        if bq["xt"].shape == bk["xt"].shape:
+            wsx = torch.empty(lmr.workspace_bytes(bq["B"], bq["H"], bq["n"]), dtype=torch.uint8, device=dev)
+            dyq = torch.empty_like(bq["dx"])
+
+            def cross_step():
+                lmr.xy_loss(bq["xt"], bq["xs"], bk["xt"], bk["xs"], scale, True, 1.0, workspace=wsx,
+                            out=bq["loss"], dx=bq["dx"], dy=dyq)
+            for _ in range(args.warmup):
+                cross_step()
+            torch.cuda.synchronize()
+            s4, e4 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s4.record()
+            for _ in range(args.steps):
+                cross_step()
+            e4.record()
+            torch.cuda.synchronize()
+            ms_x = s4.elapsed_time(e4) / args.steps
+            cross = {"ms_per_map": round(ms_x, 4),
+                     "tflops": round(6 * units(bq) / (ms_x * 1e-3) / 1e12, 3),
+                     "pct_bf16_peak": round(100 * 6 * units(bq) / (ms_x * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     "loss": float(bq["loss"].cpu()),
+                     "what": "query/key relation (X=Q, Y=K) via larard_xy_loss: LSE, row KL, dX_s and dY_s; "
+                             "6 GEMM-units per head"}
+            del wsx, dyq
+    return fwd_info, proj, cross, fused_info
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -317,109 +441,9 @@ def main():
         return b["B"] * b["H"] * 2 * b["d"] * causal_pairs(b["n"])
     step_flops = sum(6 * units(b) for b in bufs)
 
-    # Forward-only loss (one phase-1 sweep with the KL accumulator + reduce),
-    # timed the same way: 2 GEMM-units per head-map.
-    def fwd_step():
-        for b in bufs:
-            lmr.kl_fwd(b["xt"], b["xs"], scale, True, b["lse_t"], b["lse_s"], b["row_kl"])
-            lmr.reduce_loss(b["row_kl"], b["partials"], b["loss"], 1.0)
-    for _ in range(args.warmup):
-        fwd_step()
-    torch.cuda.synchronize()
-    s3, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s3.record()
-    for _ in range(args.steps):
-        fwd_step()
-    e3.record()
-    torch.cuda.synchronize()
-    ms_fwd = s3.elapsed_time(e3) / args.steps
-    losses_fwd = {b["name"]: float(b["loss"].cpu()) for b in bufs}
-
-    # The same step with every map in one launch per phase (larard_multi_loss).
-    wsm = torch.empty(lmr.multi_workspace_bytes([(b["xt"], b["xs"], 1.0, b["dx"]) for b in bufs]),
-                      dtype=torch.uint8, device=dev)
-    mlist = [(b["xt"], b["xs"], 1.0, b["dx"]) for b in bufs]
-    mloss = torch.empty((), dtype=torch.float32, device=dev)
-
-    def fused_step():
-        lmr.multi_loss(mlist, scale, True, 1.0, workspace=wsm, out=mloss)
-    for _ in range(args.warmup):
-        fused_step()
-    torch.cuda.synchronize()
-    s5, e5 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s5.record()
-    for _ in range(args.steps):
-        fused_step()
-    e5.record()
-    torch.cuda.synchronize()
-    ms_fused = s5.elapsed_time(e5) / args.steps
-    loss_fused = float(mloss.cpu())
-    del wsm
-
-    # Projection backward of the first map: dW = h^T R^T(dX_s) with synthetic
-    # bf16 hidden states of model width H*d and the student rotation (PI).
-    proj = None
-    bq0 = bufs[0]
-    dm = bq0["H"] * bq0["d"]
-    if dm % 128 == 0:
-        g = torch.Generator(device=dev)
-        g.manual_seed(1234)
-        hst = torch.randn((bq0["B"], bq0["n"], dm), generator=g, device=dev).to(torch.bfloat16)
-        pos = torch.arange(bq0["n"], dtype=torch.float64) / (w.factor if w.kind == "pi" else 1.0)
-        inv = (w.base * (w.factor ** (bq0["d"] / (bq0["d"] - 2)) if w.kind == "ntk" else w.base)) ** (
-            -2.0 * torch.arange(bq0["d"] // 2, dtype=torch.float64) / bq0["d"])
-        ang = torch.outer(pos, inv)
-        rc, rs = torch.cos(ang).float().to(dev), torch.sin(ang).float().to(dev)
-        wsp = torch.empty(int(lmr.load().larard_proj_bwd_workspace_bytes(bq0["B"], bq0["n"], dm, bq0["H"], bq0["d"])),
-                          dtype=torch.uint8, device=dev)
-        dW = torch.empty((dm, dm), dtype=torch.float32, device=dev)
-        for _ in range(args.warmup):
-            lmr.proj_bwd(hst, bq0["dx"], rc, rs, workspace=wsp, out=dW)
-        torch.cuda.synchronize()
-        s6, e6 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s6.record()
-        for _ in range(args.steps):
-            lmr.proj_bwd(hst, bq0["dx"], rc, rs, workspace=wsp, out=dW)
-        e6.record()
-        torch.cuda.synchronize()
-        ms_p = s6.elapsed_time(e6) / args.steps
-        pflops = 2.0 * dm * dm * bq0["B"] * bq0["n"]
-        proj = {"ms": round(ms_p, 4), "tflops": round(pflops / (ms_p * 1e-3) / 1e12, 3),
-                "pct_bf16_peak": round(100 * pflops / (ms_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                "what": f"larard_proj_bwd for map {bq0['name']}: dW [{dm}x{dm}] = h^T R^T(dX_s), "
-                        f"K = B*n = {bq0['B'] * bq0['n']}; synthetic bf16 h; flops 2*dm*H*d*B*n"}
-        del hst, wsp, dW
-
-    # General relation X != Y on the same data: the query/key map (X = Q,
-    # Y = K), fwd+bwd through one larard_xy_loss call (dX_s and dY_s).
-    cross = None
-    names = [b["name"] for b in bufs]
-    if "Q" in names and "K" in names:
-        bq, bk = bufs[names.index("Q")], bufs[names.index("K")]
-        if bq["xt"].shape == bk["xt"].shape:
-            wsx = torch.empty(lmr.workspace_bytes(bq["B"], bq["H"], bq["n"]), dtype=torch.uint8, device=dev)
-            dyq = torch.empty_like(bq["dx"])
-
-            def cross_step():
-                lmr.xy_loss(bq["xt"], bq["xs"], bk["xt"], bk["xs"], scale, True, 1.0, workspace=wsx,
-                            out=bq["loss"], dx=bq["dx"], dy=dyq)
-            for _ in range(args.warmup):
-                cross_step()
-            torch.cuda.synchronize()
-            s4, e4 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s4.record()
-            for _ in range(args.steps):
-                cross_step()
-            e4.record()
-            torch.cuda.synchronize()
-            ms_x = s4.elapsed_time(e4) / args.steps
-            cross = {"ms_per_map": round(ms_x, 4),
-                     "tflops": round(6 * units(bq) / (ms_x * 1e-3) / 1e12, 3),
-                     "pct_bf16_peak": round(100 * 6 * units(bq) / (ms_x * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                     "loss": float(bq["loss"].cpu()),
-                     "what": "query/key relation (X=Q, Y=K) via larard_xy_loss: LSE, row KL, dX_s and dY_s; "
-                             "6 GEMM-units per head"}
-            del wsx, dyq
+    fwd_info, proj, cross, fused_info = None, None, None, None
+    if not args.core_only:
+        fwd_info, proj, cross, fused_info = extra_sections(args, bufs, w, scale, dev, units, step_flops)
 
     # Algorithmic work.  Per head-map P = n(n+1)/2 unmasked pairs, one
     # contraction = 2*d*P flops.  Phase 1: 2 contractions; the row sweep
@@ -471,18 +495,10 @@ def main():
                    "bhn_bound_bytes": int(sum(20 * b["B"] * b["H"] * b["n"] for b in bufs)),
                    "dense_fp32_map_bytes_one_matrix": int(sum(4 * b["B"] * b["H"] * b["n"] ** 2 for b in bufs))},
         "losses": losses,
-        "forward_only": {"ms_per_step": round(ms_fwd, 4),
-                         "tflops": round(sum(2 * units(b) for b in bufs) / (ms_fwd * 1e-3) / 1e12, 3),
-                         "pct_bf16_peak": round(100 * sum(2 * units(b) for b in bufs) / (ms_fwd * 1e-3) / 1e12
-                                                / PEAK_BF16_TFLOPS, 2),
-                         "losses": losses_fwd,
-                         "what": "larard_kl_fwd + reduce per map; algorithmic flops 2 GEMM-units per head-map"},
+        "forward_only": fwd_info,
         "cross_relation": cross,
         "proj_bwd": proj,
-        "fused_maps": {"ms_per_step": round(ms_fused, 4),
-                       "tflops": round(step_flops / (ms_fused * 1e-3) / 1e12, 3),
-                       "loss_sum": loss_fused,
-                       "what": "all maps in one launch per phase (larard_multi_loss, weights 1)"},
+        "fused_maps": fused_info,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, maps, args.cpu_sample_n)
