@@ -49,9 +49,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kLog2eD = 1.4426950408889634074;
 constexpr double kLn2D = 0.69314718055994530942;
 
-constexpr int kW = 4;                  // waves per workgroup
-constexpr int kNT = 64 * kW;           // threads per workgroup
-constexpr int kOwn = 32 * kW;          // owned rows per workgroup
+// Waves per workgroup of each sweep (a workgroup of NW waves owns 32*NW
+// rows).  Eight waves halve the tile copies per owned row; the column sweep
+// measured faster with four.
+#ifndef LMR_W_LSE
+#define LMR_W_LSE 8
+#endif
+#ifndef LMR_W_ROW
+#define LMR_W_ROW 8
+#endif
+#ifndef LMR_W_COL
+#define LMR_W_COL 4
+#endif
+constexpr int kW = 4;                  // default wave count of the tile copy helpers
 constexpr int kSW = 64;                // swept rows per LDS tile
 
 enum : int { ROLE_ROW = 0, ROLE_COL = 1 };
@@ -135,8 +145,10 @@ struct Tile {
   // clamped to row n-1 and masked later).  Every wave-instruction writes 1 KB
   // of consecutive LDS (16 bytes per lane, at base + 16*lane); each lane
   // fetches the logical chunk that the swizzle puts at its physical slot.
+  template <int NW = kW>
   __device__ static inline void load(char* lds, const char* g, int row0, int n, int wave, int lane) {
-    constexpr int U = BYTES / 1024 / kW;          // instructions per wave
+    constexpr int U = BYTES / 1024 / NW;          // instructions per wave
+    static_assert(U * 1024 * NW == BYTES, "tile copy split");
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int blk = (wave * U + u) * 1024;
@@ -309,6 +321,91 @@ __device__ inline WorkItem decode(const MapSet& S, int nblk) {
   return w;
 }
 
+// End of a phase-1 sweep, shared by both sweep schedules: combine the lane
+// pair, store LSE (and row KL), or, if any row of the workgroup overflowed the
+// fixed shift, redo the workgroup's rows with the online maximum.  lds holds
+// at least two double-buffer slots of two tiles; the caller has drained its
+// own tile copies.
+template <int D, bool KL, int NW = kW>
+__device__ inline void lse_finish(const SweepArgs& a, int64_t bh, const char* yt, const char* ys,
+                                  char (*lds)[2][Tile<D>::BYTES], const bf16x8* Bt, const bf16x8* Bs, int ntiles,
+                                  int wown0, int i, int n, float c, float ref_t, float ref_s, int wave, int lane,
+                                  int h, double lsum_t, double lsum_s, double wkl) {
+  lsum_t += __shfl_xor(lsum_t, 32);
+  lsum_s += __shfl_xor(lsum_s, 32);
+  if (KL) wkl += __shfl_xor(wkl, 32);
+  const bool bad = i < n && !(lsum_t > 0.0 && lsum_t < 1e300 && lsum_s > 0.0 && lsum_s < 1e300 &&
+                              (!KL || fabs(wkl) < 1e300));
+  if (!__syncthreads_or(bad)) {
+    // LSE = ln2 * (ref + log2 L), in fp64.
+    if (h == 0 && i < n) {
+      const double l2t = log2(lsum_t), l2s = log2(lsum_s);
+      static_cast<double*>(a.lse_t)[bh * n + i] = ((double)ref_t + l2t) * kLn2D;
+      static_cast<double*>(a.lse_s)[bh * n + i] = ((double)ref_s + l2s) * kLn2D;
+      if (KL) a.row_kl[bh * n + i] = (float)((wkl / lsum_t + (l2s - l2t)) * kLn2D);
+    }
+    return;
+  }
+
+  // Fallback: online maximum.
+  float mt = -INFINITY, ms = -INFINITY;
+  lsum_t = 0.0;
+  lsum_s = 0.0;
+  for (int tI = 0; tI < ntiles; ++tI) {
+    const int buf = tI & 1, sw0 = tI * kSW;
+    __syncthreads();
+    Tile<D>::template load<NW>(lds[buf][0], yt, sw0, n, wave, lane);
+    Tile<D>::template load<NW>(lds[buf][1], ys, sw0, n, wave, lane);
+    wait_loads();
+    __syncthreads();
+    if (a.causal && sw0 > wown0 + 31) continue;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x16 St, Ss;
+      logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
+      lse_block<true>(St, Ss, c, sw0 + 32 * sb, i, n, a.causal, h, mt, lsum_t, ms, lsum_s);
+    }
+  }
+  const float mt2 = __shfl_xor(mt, 32), ms2 = __shfl_xor(ms, 32);
+  const double lt2 = __shfl_xor(lsum_t, 32), ls2 = __shfl_xor(lsum_s, 32);
+  const float Mt = fmaxf(mt, mt2), Ms = fmaxf(ms, ms2);
+  const float Mct = Mt * c, Mcs = Ms * c;
+  // The shifts Mt*c are exact fp32 values; exp2 of their (small) differences
+  // is evaluated in fp64 so the combination adds no fp32 rounding.
+  const double Lt = lsum_t * exp2((double)fmaf(mt, c, -Mct)) + lt2 * exp2((double)fmaf(mt2, c, -Mct));
+  const double Ls = lsum_s * exp2((double)fmaf(ms, c, -Mcs)) + ls2 * exp2((double)fmaf(ms2, c, -Mcs));
+  const double L2t = (double)Mct + log2(Lt), L2s = (double)Mcs + log2(Ls);
+  if (h == 0 && i < n) {
+    static_cast<double*>(a.lse_t)[bh * n + i] = L2t * kLn2D;
+    static_cast<double*>(a.lse_s)[bh * n + i] = L2s * kLn2D;
+  }
+  if (!KL) return;
+  // KL after the fallback: a second sweep against the exact statistics,
+  // as the phase-2 row sweep forms it:
+  //   KL_i = ln2 * (2^-lo_t * sum_j 2^(a_t)(a_t - a_s) + lo_s - lo_t),
+  // a_m = c z_m - hi_m, hi_m the fp32 rounding of L2_m and lo_m the rest.
+  const float ht = (float)L2t, hs = (float)L2s;
+  const double lot = L2t - (double)ht, los = L2s - (double)hs;
+  double kacc = 0.0;
+  for (int tI = 0; tI < ntiles; ++tI) {
+    const int buf = tI & 1, sw0 = tI * kSW;
+    __syncthreads();
+    Tile<D>::template load<NW>(lds[buf][0], yt, sw0, n, wave, lane);
+    Tile<D>::template load<NW>(lds[buf][1], ys, sw0, n, wave, lane);
+    wait_loads();
+    __syncthreads();
+    if (a.causal && sw0 > wown0 + 31) continue;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x16 St, Ss;
+      logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
+      kl_block_stat(St, Ss, c, ht, hs, sw0 + 32 * sb, i, n, a.causal, h, kacc);
+    }
+  }
+  kacc += __shfl_xor(kacc, 32);
+  if (h == 0 && i < n) a.row_kl[bh * n + i] = (float)((exp2(-lot) * kacc + los - lot) * kLn2D);
+}
+
 // Phase 1.  Every row's sum is taken against a fixed shift, the row's own
 // diagonal logit c*|x_i|^2 (the diagonal is always a kept entry), so the
 // inner loop needs no running maximum.  A term can only overflow if
@@ -323,9 +420,9 @@ __device__ inline WorkItem decode(const MapSet& S, int nblk) {
 // because log2 r_m = a_m - log2 L_m.  The loss then costs 2 GEMM-units
 // instead of phase 1 plus a phase-2 sweep.  Identical inputs give a_t == a_s
 // and L_t == L_s bit for bit, hence exactly zero.
-template <int D, bool KL>
-__global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(MapSet maps, int nblk) {
-  constexpr int KS = D / 16, RB = 2 * D, TB = Tile<D>::BYTES;
+template <int D, bool KL, int NW>
+__global__ __launch_bounds__(64 * NW, LMR_LSE_OCC) void lse_fwd_kernel(MapSet maps, int nblk) {
+  constexpr int KS = D / 16, RB = 2 * D, TB = Tile<D>::BYTES, kOwn = 32 * NW;
   __shared__ __attribute__((aligned(1024))) char lds[2][2][TB];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
@@ -383,15 +480,15 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(MapSet maps, 
   const float ref_t = nt * c, ref_s = ns * c;
 
   double lsum_t = 0.0, lsum_s = 0.0, wkl = 0.0;
-  Tile<D>::load(lds[0][0], yt, 0, n, wave, lane);
-  Tile<D>::load(lds[0][1], ys, 0, n, wave, lane);
+  Tile<D>::template load<NW>(lds[0][0], yt, 0, n, wave, lane);
+  Tile<D>::template load<NW>(lds[0][1], ys, 0, n, wave, lane);
   for (int tI = 0; tI < ntiles; ++tI) {
     const int buf = tI & 1, sw0 = tI * kSW;
     wait_loads();
     __syncthreads();
     if (tI + 1 < ntiles) {
-      Tile<D>::load(lds[buf ^ 1][0], yt, sw0 + kSW, n, wave, lane);
-      Tile<D>::load(lds[buf ^ 1][1], ys, sw0 + kSW, n, wave, lane);
+      Tile<D>::template load<NW>(lds[buf ^ 1][0], yt, sw0 + kSW, n, wave, lane);
+      Tile<D>::template load<NW>(lds[buf ^ 1][1], ys, sw0 + kSW, n, wave, lane);
     }
     if (a.causal && sw0 > wown0 + 31) continue;          // tile fully above the diagonal
     const bool need_mask = (a.causal && sw0 + kSW - 1 > wown0) || (sw0 + kSW > n);
@@ -405,79 +502,8 @@ __global__ __launch_bounds__(kNT, LMR_LSE_OCC) void lse_fwd_kernel(MapSet maps, 
         lse_block_fixed<false, KL>(St, Ss, c, ref_t, ref_s, sw0 + 32 * sb, i, n, a.causal, h, lsum_t, lsum_s, wkl);
     }
   }
-  lsum_t += __shfl_xor(lsum_t, 32);
-  lsum_s += __shfl_xor(lsum_s, 32);
-  if (KL) wkl += __shfl_xor(wkl, 32);
-  const bool bad = i < n && !(lsum_t > 0.0 && lsum_t < 1e300 && lsum_s > 0.0 && lsum_s < 1e300 &&
-                              (!KL || fabs(wkl) < 1e300));
-  if (!__syncthreads_or(bad)) {
-    // LSE = ln2 * (ref + log2 L), in fp64.
-    if (h == 0 && i < n) {
-      const double l2t = log2(lsum_t), l2s = log2(lsum_s);
-      static_cast<double*>(a.lse_t)[bh * n + i] = ((double)ref_t + l2t) * kLn2D;
-      static_cast<double*>(a.lse_s)[bh * n + i] = ((double)ref_s + l2s) * kLn2D;
-      if (KL) a.row_kl[bh * n + i] = (float)((wkl / lsum_t + (l2s - l2t)) * kLn2D);
-    }
-    return;
-  }
-
-  // Fallback: online maximum.
-  float mt = -INFINITY, ms = -INFINITY;
-  lsum_t = 0.0;
-  lsum_s = 0.0;
-  for (int tI = 0; tI < ntiles; ++tI) {
-    const int buf = tI & 1, sw0 = tI * kSW;
-    __syncthreads();
-    Tile<D>::load(lds[buf][0], yt, sw0, n, wave, lane);
-    Tile<D>::load(lds[buf][1], ys, sw0, n, wave, lane);
-    wait_loads();
-    __syncthreads();
-    if (a.causal && sw0 > wown0 + 31) continue;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      f32x16 St, Ss;
-      logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
-      lse_block<true>(St, Ss, c, sw0 + 32 * sb, i, n, a.causal, h, mt, lsum_t, ms, lsum_s);
-    }
-  }
-  const float mt2 = __shfl_xor(mt, 32), ms2 = __shfl_xor(ms, 32);
-  const double lt2 = __shfl_xor(lsum_t, 32), ls2 = __shfl_xor(lsum_s, 32);
-  const float Mt = fmaxf(mt, mt2), Ms = fmaxf(ms, ms2);
-  const float Mct = Mt * c, Mcs = Ms * c;
-  // The shifts Mt*c are exact fp32 values; exp2 of their (small) differences
-  // is evaluated in fp64 so the combination adds no fp32 rounding.
-  const double Lt = lsum_t * exp2((double)fmaf(mt, c, -Mct)) + lt2 * exp2((double)fmaf(mt2, c, -Mct));
-  const double Ls = lsum_s * exp2((double)fmaf(ms, c, -Mcs)) + ls2 * exp2((double)fmaf(ms2, c, -Mcs));
-  const double L2t = (double)Mct + log2(Lt), L2s = (double)Mcs + log2(Ls);
-  if (h == 0 && i < n) {
-    static_cast<double*>(a.lse_t)[bh * n + i] = L2t * kLn2D;
-    static_cast<double*>(a.lse_s)[bh * n + i] = L2s * kLn2D;
-  }
-  if (!KL) return;
-  // KL after the fallback: a second sweep against the exact statistics,
-  // as the phase-2 row sweep forms it:
-  //   KL_i = ln2 * (2^-lo_t * sum_j 2^(a_t)(a_t - a_s) + lo_s - lo_t),
-  // a_m = c z_m - hi_m, hi_m the fp32 rounding of L2_m and lo_m the rest.
-  const float ht = (float)L2t, hs = (float)L2s;
-  const double lot = L2t - (double)ht, los = L2s - (double)hs;
-  double kacc = 0.0;
-  for (int tI = 0; tI < ntiles; ++tI) {
-    const int buf = tI & 1, sw0 = tI * kSW;
-    __syncthreads();
-    Tile<D>::load(lds[buf][0], yt, sw0, n, wave, lane);
-    Tile<D>::load(lds[buf][1], ys, sw0, n, wave, lane);
-    wait_loads();
-    __syncthreads();
-    if (a.causal && sw0 > wown0 + 31) continue;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      f32x16 St, Ss;
-      logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
-      kl_block_stat(St, Ss, c, ht, hs, sw0 + 32 * sb, i, n, a.causal, h, kacc);
-    }
-  }
-  kacc += __shfl_xor(kacc, 32);
-  if (h == 0 && i < n) a.row_kl[bh * n + i] = (float)((exp2(-lot) * kacc + los - lot) * kLn2D);
+  lse_finish<D, KL, NW>(a, bh, yt, ys, lds, Bt, Bs, ntiles, wown0, i, n, c, ref_t, ref_s, wave, lane, h, lsum_t, lsum_s,
+                    wkl);
 }
 
 // ---------------------------------------------------------------------------
@@ -560,9 +586,9 @@ __device__ inline void block_elementwise(f32x16& St, const f32x16& Ss, float c, 
   }
 }
 
-template <int D, int ROLE, bool WITH_DX>
-__global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(MapSet maps, int nblk) {
-  constexpr int KS = D / 16, DB = D / 32, RB = 2 * D, TB = Tile<D>::BYTES;
+template <int D, int ROLE, bool WITH_DX, int NW>
+__global__ __launch_bounds__(64 * NW, LMR_SWEEP_OCC) void kl_sweep_kernel(MapSet maps, int nblk) {
+  constexpr int KS = D / 16, DB = D / 32, RB = 2 * D, TB = Tile<D>::BYTES, kOwn = 32 * NW;
   constexpr int NSTAT = ROLE == ROLE_COL ? 2 : 1;
   __shared__ __attribute__((aligned(1024))) char lds[2][2][TB];
   // COL: per swept row (hi_t, hi_s), double-buffered.
@@ -629,8 +655,8 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(MapSet map
     lstat[b][tid] = make_float2(ht, hs);
   };
 
-  Tile<D>::load(lds[0][0], wt, t_begin * kSW, n, wave, lane);
-  Tile<D>::load(lds[0][1], ws, t_begin * kSW, n, wave, lane);
+  Tile<D>::template load<NW>(lds[0][0], wt, t_begin * kSW, n, wave, lane);
+  Tile<D>::template load<NW>(lds[0][1], ws, t_begin * kSW, n, wave, lane);
   if (ROLE == ROLE_COL && tid < kSW) {
     fetch_stat(t_begin);
     put_stat(0, t_begin);
@@ -641,8 +667,8 @@ __global__ __launch_bounds__(kNT, LMR_SWEEP_OCC) void kl_sweep_kernel(MapSet map
     wait_loads();
     __syncthreads();
     if (tI + 1 < t_end) {
-      Tile<D>::load(lds[buf ^ 1][0], wt, sw0 + kSW, n, wave, lane);
-      Tile<D>::load(lds[buf ^ 1][1], ws, sw0 + kSW, n, wave, lane);
+      Tile<D>::template load<NW>(lds[buf ^ 1][0], wt, sw0 + kSW, n, wave, lane);
+      Tile<D>::template load<NW>(lds[buf ^ 1][1], ws, sw0 + kSW, n, wave, lane);
       if (ROLE == ROLE_COL && tid < kSW) {
         put_stat(buf ^ 1, tI + 1);
         if (tI + 2 < t_end) fetch_stat(tI + 2);
@@ -863,7 +889,7 @@ __global__ void zero_scalar_kernel(float* p) { *p = 0.f; }
 // ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
-inline int blocks_per_head(int n) { return (n + kOwn - 1) / kOwn; }
+inline int blocks_per_head(int n, int nw) { return (n + 32 * nw - 1) / (32 * nw); }
 
 MapSet single(const SweepArgs& a) {
   MapSet s{};
@@ -876,21 +902,24 @@ MapSet single(const SweepArgs& a) {
 
 template <int D, bool KL>
 hipError_t lse_typed(const MapSet& s, hipStream_t st) {
-  const int nb = blocks_per_head(s.map[0].n);
-  hipLaunchKernelGGL((lse_fwd_kernel<D, KL>), dim3((unsigned)(nb * s.head0[s.nmaps])), dim3(kNT), 0, st, s, nb);
+  constexpr int NW = LMR_W_LSE;
+  const int nb = blocks_per_head(s.map[0].n, NW);
+  hipLaunchKernelGGL((lse_fwd_kernel<D, KL, NW>), dim3((unsigned)(nb * s.head0[s.nmaps])), dim3(64 * NW), 0, st, s,
+                     nb);
   return hipGetLastError();
 }
 
 template <int D, int ROLE>
 hipError_t sweep_typed(const MapSet& s, hipStream_t st) {
+  constexpr int NW = ROLE == ROLE_ROW ? LMR_W_ROW : LMR_W_COL;
   const SweepArgs& a = s.map[0];
-  const int nb = blocks_per_head(a.n);
-  const dim3 grid((unsigned)(nb * s.head0[s.nmaps])), block(kNT);
+  const int nb = blocks_per_head(a.n, NW);
+  const dim3 grid((unsigned)(nb * s.head0[s.nmaps])), block(64 * NW);
   const bool contract = ROLE == ROLE_COL && a.cross ? a.dy != nullptr : a.dx != nullptr;
   if (contract)
-    hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, true>), grid, block, 0, st, s, nb);
+    hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, true, NW>), grid, block, 0, st, s, nb);
   else
-    hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, false>), grid, block, 0, st, s, nb);
+    hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, false, NW>), grid, block, 0, st, s, nb);
   return hipGetLastError();
 }
 
