@@ -9,12 +9,13 @@
 // dZ = (R_s - R_t)/n, which it contracts with the student projections.
 //
 // Tiling used by every sweep kernel in this file
-//   * A workgroup of 4 waves owns 128 consecutive rows of one head; wave w
+//   * A workgroup of NW waves owns 32*NW consecutive rows of one head; wave w
 //     owns 32 of them.  The owned rows' projections sit in registers as MFMA
 //     B operands for the whole sweep.
 //   * The other index ("swept") advances in tiles of 64 rows that are copied
 //     global -> LDS directly (no staging registers), double-buffered, one
-//     barrier per tile.  Each tile is processed in two 32-row sub-blocks.
+//     barrier per tile, the copy split over the NW waves.  Each tile is
+//     processed in two 32-row sub-blocks.
 //   * Logit tiles are computed swept-major: C[swept][owned] =
 //     sum_k X[swept][k] X[owned][k] with v_mfma_f32_32x32x16_bf16, so each
 //     lane holds one owned index and 16 swept indices per 32x32 block.  Row
@@ -61,23 +62,13 @@ constexpr double kLn2D = 0.69314718055994530942;
 #ifndef LMR_W_COL
 #define LMR_W_COL 4
 #endif
-constexpr int kW = 4;                  // default wave count of the tile copy helpers
 constexpr int kSW = 64;                // swept rows per LDS tile
 
 enum : int { ROLE_ROW = 0, ROLE_COL = 1 };
 
-// Build-time tuning switches (see the tile loop of kl_sweep_kernel).
-#ifndef LMR_SWEEP_PIPE
-#define LMR_SWEEP_PIPE 0          // software-pipeline unmasked tiles
-#endif
+// Minimum waves per SIMD the sweeps are compiled for (register budget 512/occ).
 #ifndef LMR_SWEEP_OCC
-#define LMR_SWEEP_OCC 2           // minimum waves per SIMD the sweep is compiled for
-#endif
-#ifndef LMR_PIPE_V1
-#define LMR_PIPE_V1 10            // VALU instructions per logit MFMA in the pipeline
-#endif
-#ifndef LMR_PIPE_V2
-#define LMR_PIPE_V2 20            // VALU instructions per contraction MFMA
+#define LMR_SWEEP_OCC 2
 #endif
 #ifndef LMR_LSE_OCC
 #define LMR_LSE_OCC 2
@@ -145,7 +136,7 @@ struct Tile {
   // clamped to row n-1 and masked later).  Every wave-instruction writes 1 KB
   // of consecutive LDS (16 bytes per lane, at base + 16*lane); each lane
   // fetches the logical chunk that the swizzle puts at its physical slot.
-  template <int NW = kW>
+  template <int NW>
   __device__ static inline void load(char* lds, const char* g, int row0, int n, int wave, int lane) {
     constexpr int U = BYTES / 1024 / NW;          // instructions per wave
     static_assert(U * 1024 * NW == BYTES, "tile copy split");
@@ -326,7 +317,7 @@ __device__ inline WorkItem decode(const MapSet& S, int nblk) {
 // fixed shift, redo the workgroup's rows with the online maximum.  lds holds
 // at least two double-buffer slots of two tiles; the caller has drained its
 // own tile copies.
-template <int D, bool KL, int NW = kW>
+template <int D, bool KL, int NW>
 __device__ inline void lse_finish(const SweepArgs& a, int64_t bh, const char* yt, const char* ys,
                                   char (*lds)[2][Tile<D>::BYTES], const bf16x8* Bt, const bf16x8* Bs, int ntiles,
                                   int wown0, int i, int n, float c, float ref_t, float ref_s, int wave, int lane,
@@ -689,84 +680,16 @@ __global__ __launch_bounds__(64 * NW, LMR_SWEEP_OCC) void kl_sweep_kernel(MapSet
     const char* ls = lds[buf][1];
     const float2* stat0 = &lstat[ROLE == ROLE_COL ? buf : 0][0];
     const float2* stat1 = &lstat[ROLE == ROLE_COL ? buf : 0][ROLE == ROLE_COL ? 32 : 0];
-    if (LMR_SWEEP_PIPE && !special) {
-      // Software pipeline over the two sub-blocks in fenced stages.  Every
-      // stage first issues all of its LDS fragment reads, then interleaves
-      // its MFMAs with independent elementwise work:
-      //   0: logits(0)    1: logits(1) | elementwise(0)
-      //   2: contract(0) | elementwise(1)    3: contract(1)
-      constexpr int KS2 = KS;
-      bf16x8 At[KS2], As[KS2];
-      f32x16 St0 = {}, Ss0 = {}, St1 = {}, Ss1 = {};
-      const int rr0 = lane & 31;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) { At[ks] = Tile<D>::frag(lt, rr0, ks, h); As[ks] = Tile<D>::frag(ls, rr0, ks, h); }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) { St0 = mma(At[ks], Bt[ks], St0); Ss0 = mma(As[ks], Bs[ks], Ss0); }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) { At[ks] = Tile<D>::frag(lt, 32 + rr0, ks, h); As[ks] = Tile<D>::frag(ls, 32 + rr0, ks, h); }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) { St1 = mma(At[ks], Bt[ks], St1); Ss1 = mma(As[ks], Bs[ks], Ss1); }
-      block_elementwise<ROLE, false>(St0, Ss0, c, sw0, o, n, a.causal, h, l2t, l2s, stat0, S);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);      // all fragment reads
-#pragma unroll
-      for (int k = 0; k < 2 * KS; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, LMR_PIPE_V1, 0); // then VALU
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (WITH_DX) {
-        bf16x8 Ar[2][DB];
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) Ar[q2][db] = Tile<D>::tr_frag(ls, q2, db, lane);
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          float v[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = St0[8 * q2 + e];
-          const bf16x8 bdz = pack8(v);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = mma(Ar[q2][db], bdz, acc[db]);
-        }
-        block_elementwise<ROLE, false>(St1, Ss1, c, sw0 + 32, o, n, a.causal, h, l2t, l2s, stat1, S);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 0);     // transpose reads (2 per fragment)
-#pragma unroll
-        for (int k = 0; k < 2 * DB; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, LMR_PIPE_V2, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) Ar[q2][db] = Tile<D>::tr_frag(ls, 2 + q2, db, lane);
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          float v[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = St1[8 * q2 + e];
-          const bf16x8 bdz = pack8(v);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = mma(Ar[q2][db], bdz, acc[db]);
-        }
-      } else {
-        block_elementwise<ROLE, false>(St1, Ss1, c, sw0 + 32, o, n, a.causal, h, l2t, l2s, stat1, S);
-      }
-    } else {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        f32x16 St, Ss;
-        logits<D>(lt, ls, Bt, Bs, St, Ss, sb, lane);
-        const float2* stat = sb ? stat1 : stat0;
-        if (special)
-          block_elementwise<ROLE, true>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
-        else
-          block_elementwise<ROLE, false>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
-        if constexpr (WITH_DX) contract<D>(St, ls, sb, lane, acc);
-      }
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x16 St, Ss;
+      logits<D>(lt, ls, Bt, Bs, St, Ss, sb, lane);
+      const float2* stat = sb ? stat1 : stat0;
+      if (special)
+        block_elementwise<ROLE, true>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
+      else
+        block_elementwise<ROLE, false>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
+      if constexpr (WITH_DX) contract<D>(St, ls, sb, lane, acc);
     }
   }
 

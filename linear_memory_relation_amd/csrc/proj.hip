@@ -13,8 +13,9 @@
 //     transposed as G^T [H*d, Kp] (token index b*n + i along K, zero padded
 //     to Kp, a multiple of 64);
 //   * transpose_h_kernel: h^T [D, Kp] bf16;
-//   * gemm_nt_kernel: dW[M=D, N=H*d] = h^T G (both operands K-contiguous),
-//     bf16 MFMA with fp32 accumulation, 128x128 output tile per workgroup.
+//   * gemm_nt_kernel / gemm_nt_256_kernel: dW[M=D, N=H*d] = h^T G (both
+//     operands K-contiguous), bf16 MFMA with fp32 accumulation, a 128x128 or
+//     256x256 output tile per workgroup.
 #include <stdint.h>
 
 #include "launch.h"
@@ -99,8 +100,9 @@ __device__ inline int sw(int r) {
 }
 __device__ inline int slot_off(int r, int c) { return r * 128 + ((c ^ sw(r)) << 4); }
 
-// Copy rows row0..row0+127, K columns k0..k0+63 of a [rows, kp] matrix into
-// the tile; 4 waves x 4 instructions of 1 KB (16 B per lane).
+// Copy rows row0..row0+32*NW-1, K columns k0..k0+63 of a [rows, kp] matrix
+// into the tile; NW waves x 4 instructions of 1 KB (16 B per lane), so 4 waves
+// copy 128 rows and 8 waves 256.
 __device__ inline void load_tile(char* lds, const uint16_t* g, int64_t row0, int64_t kp, int64_t k0, int wave,
                                  int lane) {
 #pragma unroll
@@ -170,17 +172,79 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* A, cons
       }
 }
 
+// The same product with a 256 x 256 workgroup tile: 8 waves of 128 x 64 (two
+// along M, four along N), 4 x 2 blocks of 32 x 32 each.  Per 16-step a wave
+// reads 6 fragments for 8 MFMAs (the 128 x 128 kernel: 4 for 4), and every
+// copied operand row serves twice as many outputs.  128 KiB of LDS: one
+// workgroup (2 waves per SIMD) per CU.
+__global__ __launch_bounds__(512) void gemm_nt_256_kernel(const uint16_t* A, const uint16_t* Bm, int64_t kp,
+                                                          int64_t N, float* C) {
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][256 * 128];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int64_t m0 = (int64_t)blockIdx.y * 256, n0 = (int64_t)blockIdx.x * 256;
+  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 64;
+  f32x16 acc[4][2] = {};
+  const int64_t nk = kp / 64;
+  if (nk > 0) {
+    load_tile(lds[0][0], A, m0, kp, 0, wave, lane);
+    load_tile(lds[0][1], Bm, n0, kp, 0, wave, lane);
+  }
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = (int)(kt & 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 < nk) {
+      load_tile(lds[buf ^ 1][0], A, m0, kp, (kt + 1) * 64, wave, lane);
+      load_tile(lds[buf ^ 1][1], Bm, n0, kp, (kt + 1) * 64, wave, lane);
+    }
+    const char* ta = lds[buf][0];
+    const char* tb = lds[buf][1];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 fa[4], fb[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = frag(ta, wm + 32 * i + l32, ks, h);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = frag(tb, wn + 32 * j + l32, ks, h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        C[row * N + n0 + wn + 32 * j + l32] = acc[i][j][r];
+      }
+}
+
+// The 256 x 256 tile only when its grid still covers every CU (256).
+bool use_256_tiles(int64_t M, int64_t N) { return M % 256 == 0 && N % 256 == 0 && (M / 256) * (N / 256) >= 256; }
+
+hipError_t launch_gemm(const uint16_t* A, const uint16_t* Bm, int64_t kp, int64_t M, int64_t N, float* C,
+                       hipStream_t st) {
+  if (use_256_tiles(M, N))
+    hipLaunchKernelGGL(gemm_nt_256_kernel, dim3((unsigned)(N / 256), (unsigned)(M / 256)), dim3(512), 0, st, A, Bm,
+                       kp, N, C);
+  else
+    hipLaunchKernelGGL(gemm_nt_kernel, dim3((unsigned)(N / 128), (unsigned)(M / 128)), dim3(256), 0, st, A, Bm, kp,
+                       N, C);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_proj_bwd(const ProjArgs& p, hipStream_t st) {
   const int64_t ntok = p.B * p.n;
   const int64_t N = p.H * p.d;
   hipError_t e;
-  if (p.kp == 0) {   // no tokens: the GEMM runs no K step and writes dW = 0
-    hipLaunchKernelGGL(gemm_nt_kernel, dim3((unsigned)(N / 128), (unsigned)(p.dm / 128)), dim3(256), 0, st,
-                       p.ht, p.gt, p.kp, N, p.dw);
-    return hipGetLastError();
-  }
+  if (p.kp == 0)   // no tokens: the GEMM runs no K step and writes dW = 0
+    return launch_gemm(p.ht, p.gt, p.kp, p.dm, N, p.dw, st);
   const dim3 tgrid((unsigned)(p.kp / kTok), (unsigned)p.H);
   if (p.d == 64)
     hipLaunchKernelGGL(rope_t_kernel<64>, tgrid, dim3(256), 0, st, p.dx, p.cos, p.sin, p.B, (int)p.n, (int)p.H, p.kp, p.gt);
@@ -190,9 +254,7 @@ hipError_t launch_proj_bwd(const ProjArgs& p, hipStream_t st) {
   hipLaunchKernelGGL(transpose_h_kernel, dim3((unsigned)(p.kp / 64), (unsigned)(p.dm / 64)), dim3(256), 0, st,
                      p.h, ntok, p.dm, p.kp, p.ht);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(gemm_nt_kernel, dim3((unsigned)(N / 128), (unsigned)(p.dm / 128)), dim3(256), 0, st,
-                     p.ht, p.gt, p.kp, N, p.dw);
-  return hipGetLastError();
+  return launch_gemm(p.ht, p.gt, p.kp, p.dm, N, p.dw, st);
 }
 
 }  // namespace lmr

@@ -22,13 +22,20 @@ def _tables32(n, d, base=1.0e4, pos_scale=8.0):
 
 
 def _g_bf16(dx32, c32, s32):
-    """G = R^T dX in fp32 as the kernel forms it, rounded once to bf16 (fp64 image)."""
+    """G = R^T dX in fp32 in the kernel's operation order, rounded once to bf16
+    (fp64 image): g1 = fma(y1, c, fp32(y2 s)), g2 = fma(y2, c, -fp32(y1 s)).  The
+    fma is exact in fp64 (an fp32 product is exact there) up to the final fp32
+    rounding."""
     if c32 is None:
         g = dx32.astype(np.float32)
     else:
         half = dx32.shape[-1] // 2
-        y1, y2 = dx32[..., :half], dx32[..., half:]
-        g = np.concatenate([np.float32(y1 * c32 + y2 * s32), np.float32(y2 * c32 - y1 * s32)], axis=-1)
+        y1 = dx32[..., :half].astype(np.float64)
+        y2 = dx32[..., half:].astype(np.float64)
+        c64, s64 = c32.astype(np.float64), s32.astype(np.float64)
+        t1 = si.round_f32(y2 * s64).astype(np.float64)
+        t2 = si.round_f32(y1 * s64).astype(np.float64)
+        g = np.concatenate([si.round_f32(y1 * c64 + t1), si.round_f32(y2 * c64 - t2)], axis=-1)
     return si.bf16_bits_to_f64(si.round_bf16_bits(g.astype(np.float64)))
 
 
@@ -52,6 +59,12 @@ def test_proj_bwd_small(gpu_lib, B, n, dm, H, d, rope):
     g = _g_bf16(dx, c, s)
     same_rounding = oracle.proj_bwd(h64, g)
     assert normwise_max_rel(got, same_rounding) < 1e-4
+
+
+def test_proj_bwd_256_tiles_ragged_tokens(gpu_lib):
+    """d_model = H*d = 4096 takes the 256 x 256 workgroup tile; B*n = 200
+    tokens leave a ragged, zero-padded last K step."""
+    test_proj_bwd_small(gpu_lib, 2, 100, 4096, 32, 128, True)
 
 
 def test_proj_bwd_empty_sequence_writes_zeros(gpu_lib):
