@@ -18,7 +18,9 @@ thread_local std::string g_last_error;
 
 constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
-constexpr int kOwnRows = 128;   // rows owned by one workgroup (see kernels.hip)
+// Fewest rows any sweep kernel assigns to one workgroup (the fp32 kernels own
+// 32; the bf16 kernels 128 or 256), so B*H*ceil(n/kOwnRows) bounds every grid.
+constexpr int kOwnRows = 32;
 
 larard_status fail(larard_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 larard_status fail(larard_status st, const char* fmt, ...) {
@@ -50,7 +52,7 @@ larard_status check_common(const void* x_t, const void* x_s, larard_dtype dtype,
   if (B > kMaxGrid / H) return fail(LARARD_E_INVALID, "B*H too large");
   const int64_t bh = B * H;
   const int64_t nblk = (n + kOwnRows - 1) / kOwnRows;
-  if (nblk > 0 && bh > kMaxGrid / nblk) return fail(LARARD_E_INVALID, "B*H*ceil(n/128) exceeds the launch grid");
+  if (nblk > 0 && bh > kMaxGrid / nblk) return fail(LARARD_E_INVALID, "B*H*ceil(n/32) exceeds the launch grid");
   if (dtype != LARARD_BF16 && dtype != LARARD_FP32) return fail(LARARD_E_UNSUPPORTED, "dtype %d not supported", (int)dtype);
   if (d != 64 && d != 128) return fail(LARARD_E_UNSUPPORTED, "head dim d=%lld not supported (64 or 128)", (long long)d);
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(LARARD_E_INVALID, "scale must be finite and > 0");
@@ -425,7 +427,7 @@ larard_status larard_multi_loss(const larard_map* maps, int n_maps, larard_dtype
   if (heads > kMaxGrid / B) return fail(LARARD_E_INVALID, "B * sum of heads too large");
   const int64_t bh_all = B * heads;
   const int64_t nblk = (n + kOwnRows - 1) / kOwnRows;
-  if (nblk > 0 && bh_all > kMaxGrid / nblk) return fail(LARARD_E_INVALID, "B*sum(H)*ceil(n/128) exceeds the launch grid");
+  if (nblk > 0 && bh_all > kMaxGrid / nblk) return fail(LARARD_E_INVALID, "B*sum(H)*ceil(n/32) exceeds the launch grid");
   if (!std::isfinite(loss_scale)) return fail(LARARD_E_INVALID, "loss_scale must be finite");
   if (loss == nullptr || !aligned(loss, 4)) return fail(LARARD_E_INVALID, "loss must be a 4-byte aligned device pointer");
   const hipStream_t st = static_cast<hipStream_t>(stream);

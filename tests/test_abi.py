@@ -73,6 +73,8 @@ def _lse(lib, **kw):
     (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(scale=0.0), 1),
     (dict(scale=-0.5), 1), (dict(lt=None), 1), (dict(ls=FAKE + 2), 1),
     (dict(dt=1, lt=FAKE + 4), 1), (dict(lt=FAKE + 4), 1),   # fp64 statistics: 8-byte alignment
+    # fp32 kernels own 32 rows per workgroup: 8192 heads x 2^19 row blocks overflow the grid
+    (dict(dt=1, H=1 << 13, n=1 << 24), 1), (dict(H=1 << 13, n=1 << 24), 1),
 ])
 def test_lse_fwd_validation(lib, kw, code):
     assert _lse(lib, **kw) == code
