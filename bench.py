@@ -332,7 +332,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this kernel shards by heads "
-              f"with no exchange but a scalar loss sum, and multi-GPU runs are not part of this build.",
+              f"with no exchange but a scalar loss sum; this benchmark measures a single GPU.",
               file=sys.stderr)
         sys.exit(2)
 
