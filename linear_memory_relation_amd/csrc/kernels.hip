@@ -62,7 +62,19 @@ constexpr double kLn2D = 0.69314718055994530942;
 #ifndef LMR_W_COL
 #define LMR_W_COL 4
 #endif
-constexpr int kSW = 64;                // swept rows per LDS tile
+// Swept rows per LDS tile of each sweep (a multiple of 32).  128-row tiles
+// halve the tile waits and barriers per block; the 8-wave sweeps have the LDS
+// for them (2 x 2 x 32 KiB, one workgroup per CU).  The 4-wave column sweep
+// keeps 64 rows, so that two of its workgroups share a CU.
+#ifndef LMR_SW_LSE
+#define LMR_SW_LSE 128
+#endif
+#ifndef LMR_SW_ROW
+#define LMR_SW_ROW 128
+#endif
+#ifndef LMR_SW_COL
+#define LMR_SW_COL 64
+#endif
 
 enum : int { ROLE_ROW = 0, ROLE_COL = 1 };
 
@@ -99,14 +111,14 @@ __device__ inline void split_stat(double lse_nat, float& hi, float& lo) {
 // in 16 distinct bank groups) and maps 4 consecutive rows to 4 different
 // 4-chunk blocks (so the 4 rows x 4 chunks of a transpose read are
 // conflict free as well).
-template <int D>
+template <int D, int SW = 64>
 struct Tile {
   static constexpr int RB = 2 * D;                // bytes per row
   static constexpr int CH = RB / 16;              // chunks per row: 8 or 16
   static constexpr int RPL = 256 / RB;            // rows per 256-byte bank line
   static constexpr int QB = CH / 4;
   static constexpr int QSH = QB == 4 ? 2 : 1;
-  static constexpr int BYTES = kSW * RB;
+  static constexpr int BYTES = SW * RB;           // one tile of SW swept rows
   static_assert(D == 64 || D == 128, "head dim");
   __device__ static inline int f(int r) {
     const int m = r / RPL;
@@ -132,7 +144,7 @@ struct Tile {
     const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
     return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  // Direct global -> LDS copy of kSW rows starting at row0 (rows >= n are
+  // Direct global -> LDS copy of SW rows starting at row0 (rows >= n are
   // clamped to row n-1 and masked later).  Every wave-instruction writes 1 KB
   // of consecutive LDS (16 bytes per lane, at base + 16*lane); each lane
   // fetches the logical chunk that the swizzle puts at its physical slot.
@@ -317,9 +329,9 @@ __device__ inline WorkItem decode(const MapSet& S, int nblk) {
 // fixed shift, redo the workgroup's rows with the online maximum.  lds holds
 // at least two double-buffer slots of two tiles; the caller has drained its
 // own tile copies.
-template <int D, bool KL, int NW>
+template <int D, bool KL, int NW, int SW>
 __device__ inline void lse_finish(const SweepArgs& a, int64_t bh, const char* yt, const char* ys,
-                                  char (*lds)[2][Tile<D>::BYTES], const bf16x8* Bt, const bf16x8* Bs, int ntiles,
+                                  char (*lds)[2][Tile<D, SW>::BYTES], const bf16x8* Bt, const bf16x8* Bs, int ntiles,
                                   int wown0, int i, int n, float c, float ref_t, float ref_s, int wave, int lane,
                                   int h, double lsum_t, double lsum_s, double wkl) {
   lsum_t += __shfl_xor(lsum_t, 32);
@@ -343,15 +355,15 @@ __device__ inline void lse_finish(const SweepArgs& a, int64_t bh, const char* yt
   lsum_t = 0.0;
   lsum_s = 0.0;
   for (int tI = 0; tI < ntiles; ++tI) {
-    const int buf = tI & 1, sw0 = tI * kSW;
+    const int buf = tI & 1, sw0 = tI * SW;
     __syncthreads();
-    Tile<D>::template load<NW>(lds[buf][0], yt, sw0, n, wave, lane);
-    Tile<D>::template load<NW>(lds[buf][1], ys, sw0, n, wave, lane);
+    Tile<D, SW>::template load<NW>(lds[buf][0], yt, sw0, n, wave, lane);
+    Tile<D, SW>::template load<NW>(lds[buf][1], ys, sw0, n, wave, lane);
     wait_loads();
     __syncthreads();
     if (a.causal && sw0 > wown0 + 31) continue;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    for (int sb = 0; sb < SW / 32; ++sb) {
       f32x16 St, Ss;
       logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
       lse_block<true>(St, Ss, c, sw0 + 32 * sb, i, n, a.causal, h, mt, lsum_t, ms, lsum_s);
@@ -379,15 +391,15 @@ __device__ inline void lse_finish(const SweepArgs& a, int64_t bh, const char* yt
   const double lot = L2t - (double)ht, los = L2s - (double)hs;
   double kacc = 0.0;
   for (int tI = 0; tI < ntiles; ++tI) {
-    const int buf = tI & 1, sw0 = tI * kSW;
+    const int buf = tI & 1, sw0 = tI * SW;
     __syncthreads();
-    Tile<D>::template load<NW>(lds[buf][0], yt, sw0, n, wave, lane);
-    Tile<D>::template load<NW>(lds[buf][1], ys, sw0, n, wave, lane);
+    Tile<D, SW>::template load<NW>(lds[buf][0], yt, sw0, n, wave, lane);
+    Tile<D, SW>::template load<NW>(lds[buf][1], ys, sw0, n, wave, lane);
     wait_loads();
     __syncthreads();
     if (a.causal && sw0 > wown0 + 31) continue;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    for (int sb = 0; sb < SW / 32; ++sb) {
       f32x16 St, Ss;
       logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
       kl_block_stat(St, Ss, c, ht, hs, sw0 + 32 * sb, i, n, a.causal, h, kacc);
@@ -411,9 +423,9 @@ __device__ inline void lse_finish(const SweepArgs& a, int64_t bh, const char* yt
 // because log2 r_m = a_m - log2 L_m.  The loss then costs 2 GEMM-units
 // instead of phase 1 plus a phase-2 sweep.  Identical inputs give a_t == a_s
 // and L_t == L_s bit for bit, hence exactly zero.
-template <int D, bool KL, int NW>
+template <int D, bool KL, int NW, int SW>
 __global__ __launch_bounds__(64 * NW, LMR_LSE_OCC) void lse_fwd_kernel(MapSet maps, int nblk) {
-  constexpr int KS = D / 16, RB = 2 * D, TB = Tile<D>::BYTES, kOwn = 32 * NW;
+  constexpr int KS = D / 16, RB = 2 * D, TB = Tile<D, SW>::BYTES, kOwn = 32 * NW;
   __shared__ __attribute__((aligned(1024))) char lds[2][2][TB];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
@@ -438,7 +450,7 @@ __global__ __launch_bounds__(64 * NW, LMR_LSE_OCC) void lse_fwd_kernel(MapSet ma
     for (int ks = 0; ks < KS; ++ks) { Bt[ks] = load_own(rt, ks, h); Bs[ks] = load_own(rs, ks, h); }
   }
   const int last = a.causal ? min(own0 + kOwn, n) - 1 : n - 1;
-  const int ntiles = last / kSW + 1;
+  const int ntiles = last / SW + 1;
   const float c = a.scale * kLog2e;
 
   // Shift: the diagonal logit c * <x_i, y_i> (c * |x_i|^2 for a self-relation),
@@ -471,29 +483,31 @@ __global__ __launch_bounds__(64 * NW, LMR_LSE_OCC) void lse_fwd_kernel(MapSet ma
   const float ref_t = nt * c, ref_s = ns * c;
 
   double lsum_t = 0.0, lsum_s = 0.0, wkl = 0.0;
-  Tile<D>::template load<NW>(lds[0][0], yt, 0, n, wave, lane);
-  Tile<D>::template load<NW>(lds[0][1], ys, 0, n, wave, lane);
+  Tile<D, SW>::template load<NW>(lds[0][0], yt, 0, n, wave, lane);
+  Tile<D, SW>::template load<NW>(lds[0][1], ys, 0, n, wave, lane);
   for (int tI = 0; tI < ntiles; ++tI) {
-    const int buf = tI & 1, sw0 = tI * kSW;
+    const int buf = tI & 1, sw0 = tI * SW;
     wait_loads();
     __syncthreads();
     if (tI + 1 < ntiles) {
-      Tile<D>::template load<NW>(lds[buf ^ 1][0], yt, sw0 + kSW, n, wave, lane);
-      Tile<D>::template load<NW>(lds[buf ^ 1][1], ys, sw0 + kSW, n, wave, lane);
+      Tile<D, SW>::template load<NW>(lds[buf ^ 1][0], yt, sw0 + SW, n, wave, lane);
+      Tile<D, SW>::template load<NW>(lds[buf ^ 1][1], ys, sw0 + SW, n, wave, lane);
     }
-    if (a.causal && sw0 > wown0 + 31) continue;          // tile fully above the diagonal
-    const bool need_mask = (a.causal && sw0 + kSW - 1 > wown0) || (sw0 + kSW > n);
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    for (int sb = 0; sb < SW / 32; ++sb) {
+      // 32-row block: stop past this wave's diagonal block or past the end.
+      const int swb = sw0 + 32 * sb;
+      if ((a.causal && swb > wown0 + 31) || swb >= n) break;
+      const bool need_mask = (a.causal && swb + 31 > wown0) || swb + 32 > n;
       f32x16 St, Ss;
       logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
       if (need_mask)
-        lse_block_fixed<true, KL>(St, Ss, c, ref_t, ref_s, sw0 + 32 * sb, i, n, a.causal, h, lsum_t, lsum_s, wkl);
+        lse_block_fixed<true, KL>(St, Ss, c, ref_t, ref_s, swb, i, n, a.causal, h, lsum_t, lsum_s, wkl);
       else
-        lse_block_fixed<false, KL>(St, Ss, c, ref_t, ref_s, sw0 + 32 * sb, i, n, a.causal, h, lsum_t, lsum_s, wkl);
+        lse_block_fixed<false, KL>(St, Ss, c, ref_t, ref_s, swb, i, n, a.causal, h, lsum_t, lsum_s, wkl);
     }
   }
-  lse_finish<D, KL, NW>(a, bh, yt, ys, lds, Bt, Bs, ntiles, wown0, i, n, c, ref_t, ref_s, wave, lane, h, lsum_t, lsum_s,
+  lse_finish<D, KL, NW, SW>(a, bh, yt, ys, lds, Bt, Bs, ntiles, wown0, i, n, c, ref_t, ref_s, wave, lane, h, lsum_t, lsum_s,
                     wkl);
 }
 
@@ -577,13 +591,14 @@ __device__ inline void block_elementwise(f32x16& St, const f32x16& Ss, float c, 
   }
 }
 
-template <int D, int ROLE, bool WITH_DX, int NW>
+template <int D, int ROLE, bool WITH_DX, int NW, int SW>
 __global__ __launch_bounds__(64 * NW, LMR_SWEEP_OCC) void kl_sweep_kernel(MapSet maps, int nblk) {
-  constexpr int KS = D / 16, DB = D / 32, RB = 2 * D, TB = Tile<D>::BYTES, kOwn = 32 * NW;
+  constexpr int KS = D / 16, DB = D / 32, RB = 2 * D, TB = Tile<D, SW>::BYTES, kOwn = 32 * NW;
+  static_assert(SW % 32 == 0 && SW <= 64 * NW, "one thread per swept row fetches the statistics");
   constexpr int NSTAT = ROLE == ROLE_COL ? 2 : 1;
   __shared__ __attribute__((aligned(1024))) char lds[2][2][TB];
   // COL: per swept row (hi_t, hi_s), double-buffered.
-  __shared__ float2 lstat[NSTAT][ROLE == ROLE_COL ? kSW : 1];
+  __shared__ float2 lstat[NSTAT][ROLE == ROLE_COL ? SW : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
   const WorkItem wi = decode(maps, nblk);
@@ -618,10 +633,10 @@ __global__ __launch_bounds__(64 * NW, LMR_SWEEP_OCC) void kl_sweep_kernel(MapSet
   int t_begin, t_end;
   if (ROLE == ROLE_ROW) {
     t_begin = 0;
-    t_end = (a.causal ? min(own0 + kOwn, n) - 1 : n - 1) / kSW + 1;
+    t_end = (a.causal ? min(own0 + kOwn, n) - 1 : n - 1) / SW + 1;
   } else {
-    t_begin = a.causal ? own0 / kSW : 0;
-    t_end = (n - 1) / kSW + 1;
+    t_begin = a.causal ? own0 / SW : 0;
+    t_end = (n - 1) / SW + 1;
   }
 
   SweepState S;
@@ -632,12 +647,12 @@ __global__ __launch_bounds__(64 * NW, LMR_SWEEP_OCC) void kl_sweep_kernel(MapSet
   // COL statistics: threads 0..63 hold the fp64 LSE of the next tile's rows.
   double nlt = 0.0, nls = 0.0;
   auto fetch_stat = [&](int tile) {
-    const int g = tile * kSW + tid;
+    const int g = tile * SW + tid;
     nlt = g < n ? glt[g] : 0.0;
     nls = g < n ? gls[g] : 0.0;
   };
   auto put_stat = [&](int b, int tile) {
-    const int g = tile * kSW + tid;
+    const int g = tile * SW + tid;
     float ht = 0.f, hs = 0.f, ft, fs;
     if (g < n) {
       split_stat(nlt, ht, ft);
@@ -646,50 +661,61 @@ __global__ __launch_bounds__(64 * NW, LMR_SWEEP_OCC) void kl_sweep_kernel(MapSet
     lstat[b][tid] = make_float2(ht, hs);
   };
 
-  Tile<D>::template load<NW>(lds[0][0], wt, t_begin * kSW, n, wave, lane);
-  Tile<D>::template load<NW>(lds[0][1], ws, t_begin * kSW, n, wave, lane);
-  if (ROLE == ROLE_COL && tid < kSW) {
+  Tile<D, SW>::template load<NW>(lds[0][0], wt, t_begin * SW, n, wave, lane);
+  Tile<D, SW>::template load<NW>(lds[0][1], ws, t_begin * SW, n, wave, lane);
+  if (ROLE == ROLE_COL && tid < SW) {
     fetch_stat(t_begin);
     put_stat(0, t_begin);
     if (t_begin + 1 < t_end) fetch_stat(t_begin + 1);
   }
   for (int tI = t_begin; tI < t_end; ++tI) {
-    const int buf = (tI - t_begin) & 1, sw0 = tI * kSW;
+    const int buf = (tI - t_begin) & 1, sw0 = tI * SW;
     wait_loads();
     __syncthreads();
     if (tI + 1 < t_end) {
-      Tile<D>::template load<NW>(lds[buf ^ 1][0], wt, sw0 + kSW, n, wave, lane);
-      Tile<D>::template load<NW>(lds[buf ^ 1][1], ws, sw0 + kSW, n, wave, lane);
-      if (ROLE == ROLE_COL && tid < kSW) {
+      Tile<D, SW>::template load<NW>(lds[buf ^ 1][0], wt, sw0 + SW, n, wave, lane);
+      Tile<D, SW>::template load<NW>(lds[buf ^ 1][1], ws, sw0 + SW, n, wave, lane);
+      if (ROLE == ROLE_COL && tid < SW) {
         put_stat(buf ^ 1, tI + 1);
         if (tI + 2 < t_end) fetch_stat(tI + 2);
       }
     }
-    bool skip, need_mask;
-    if (ROLE == ROLE_ROW) {
-      skip = a.causal && sw0 > wown0 + 31;
-      need_mask = (a.causal && sw0 + kSW - 1 > wown0) || (sw0 + kSW > n);
-    } else {
-      skip = a.causal && wown0 > sw0 + kSW - 1;
-      need_mask = (a.causal && wown0 + 31 > sw0) || (sw0 + kSW > n);
-    }
-    if (skip) continue;
-    // Tiles that hold a diagonal entry of this wave take the per-entry path too.
-    const bool special = need_mask || (sw0 <= wown0 + 31 && sw0 + kSW - 1 >= wown0);
     const char* lt = lds[buf][0];
     const char* ls = lds[buf][1];
-    const float2* stat0 = &lstat[ROLE == ROLE_COL ? buf : 0][0];
-    const float2* stat1 = &lstat[ROLE == ROLE_COL ? buf : 0][ROLE == ROLE_COL ? 32 : 0];
+    if constexpr (ROLE == ROLE_ROW) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      f32x16 St, Ss;
-      logits<D>(lt, ls, Bt, Bs, St, Ss, sb, lane);
-      const float2* stat = sb ? stat1 : stat0;
-      if (special)
-        block_elementwise<ROLE, true>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
-      else
-        block_elementwise<ROLE, false>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
-      if constexpr (WITH_DX) contract<D>(St, ls, sb, lane, acc);
+      for (int sb = 0; sb < SW / 32; ++sb) {
+        // 32-row swept block: stop past this wave's diagonal block or past
+        // the end.  Blocks with masked entries or with this wave's diagonal
+        // take the per-entry path.
+        const int swb = sw0 + 32 * sb;
+        if ((a.causal && swb > wown0 + 31) || swb >= n) break;
+        const bool need_mask = (a.causal && swb + 31 > wown0) || swb + 32 > n;
+        f32x16 St, Ss;
+        logits<D>(lt, ls, Bt, Bs, St, Ss, sb, lane);
+        if (need_mask || swb == wown0)
+          block_elementwise<ROLE, true>(St, Ss, c, swb, o, n, a.causal, h, l2t, l2s, nullptr, S);
+        else
+          block_elementwise<ROLE, false>(St, Ss, c, swb, o, n, a.causal, h, l2t, l2s, nullptr, S);
+        if constexpr (WITH_DX) contract<D>(St, ls, sb, lane, acc);
+      }
+    } else {
+      // Column sweep: decided per tile (per-block tests measured slower here).
+      if (a.causal && wown0 > sw0 + SW - 1) continue;        // tile entirely above the diagonal
+      const bool need_mask = (a.causal && wown0 + 31 > sw0) || (sw0 + SW > n);
+      // Tiles that hold a diagonal entry of this wave take the per-entry path too.
+      const bool special = need_mask || (sw0 <= wown0 + 31 && sw0 + SW - 1 >= wown0);
+#pragma unroll
+      for (int sb = 0; sb < SW / 32; ++sb) {
+        const float2* stat = &lstat[buf][32 * sb];
+        f32x16 St, Ss;
+        logits<D>(lt, ls, Bt, Bs, St, Ss, sb, lane);
+        if (special)
+          block_elementwise<ROLE, true>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
+        else
+          block_elementwise<ROLE, false>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
+        if constexpr (WITH_DX) contract<D>(St, ls, sb, lane, acc);
+      }
     }
   }
 
@@ -827,22 +853,23 @@ template <int D, bool KL>
 hipError_t lse_typed(const MapSet& s, hipStream_t st) {
   constexpr int NW = LMR_W_LSE;
   const int nb = blocks_per_head(s.map[0].n, NW);
-  hipLaunchKernelGGL((lse_fwd_kernel<D, KL, NW>), dim3((unsigned)(nb * s.head0[s.nmaps])), dim3(64 * NW), 0, st, s,
-                     nb);
+  hipLaunchKernelGGL((lse_fwd_kernel<D, KL, NW, LMR_SW_LSE>), dim3((unsigned)(nb * s.head0[s.nmaps])), dim3(64 * NW),
+                     0, st, s, nb);
   return hipGetLastError();
 }
 
 template <int D, int ROLE>
 hipError_t sweep_typed(const MapSet& s, hipStream_t st) {
   constexpr int NW = ROLE == ROLE_ROW ? LMR_W_ROW : LMR_W_COL;
+  constexpr int SW = ROLE == ROLE_ROW ? LMR_SW_ROW : LMR_SW_COL;
   const SweepArgs& a = s.map[0];
   const int nb = blocks_per_head(a.n, NW);
   const dim3 grid((unsigned)(nb * s.head0[s.nmaps])), block(64 * NW);
   const bool contract = ROLE == ROLE_COL && a.cross ? a.dy != nullptr : a.dx != nullptr;
   if (contract)
-    hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, true, NW>), grid, block, 0, st, s, nb);
+    hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, true, NW, SW>), grid, block, 0, st, s, nb);
   else
-    hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, false, NW>), grid, block, 0, st, s, nb);
+    hipLaunchKernelGGL((kl_sweep_kernel<D, ROLE, false, NW, SW>), grid, block, 0, st, s, nb);
   return hipGetLastError();
 }
 
