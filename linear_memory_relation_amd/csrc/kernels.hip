@@ -51,8 +51,7 @@ constexpr double kLog2eD = 1.4426950408889634074;
 constexpr double kLn2D = 0.69314718055994530942;
 
 // Waves per workgroup of each sweep (a workgroup of NW waves owns 32*NW
-// rows).  Eight waves halve the tile copies per owned row; the column sweep
-// measured faster with four.
+// rows).  Eight waves halve the tile copies per owned row.
 #ifndef LMR_W_LSE
 #define LMR_W_LSE 8
 #endif
@@ -60,12 +59,11 @@ constexpr double kLn2D = 0.69314718055994530942;
 #define LMR_W_ROW 8
 #endif
 #ifndef LMR_W_COL
-#define LMR_W_COL 4
+#define LMR_W_COL 8
 #endif
 // Swept rows per LDS tile of each sweep (a multiple of 32).  128-row tiles
-// halve the tile waits and barriers per block; the 8-wave sweeps have the LDS
-// for them (2 x 2 x 32 KiB, one workgroup per CU).  The 4-wave column sweep
-// keeps 64 rows, so that two of its workgroups share a CU.
+// halve the tile waits and barriers per block; an 8-wave workgroup has the
+// LDS for them (2 x 2 x 32 KiB, one workgroup per CU).
 #ifndef LMR_SW_LSE
 #define LMR_SW_LSE 128
 #endif
@@ -73,7 +71,7 @@ constexpr double kLn2D = 0.69314718055994530942;
 #define LMR_SW_ROW 128
 #endif
 #ifndef LMR_SW_COL
-#define LMR_SW_COL 64
+#define LMR_SW_COL 128
 #endif
 
 enum : int { ROLE_ROW = 0, ROLE_COL = 1 };
