@@ -12,7 +12,7 @@
 //   * rope_t_kernel: G = R^T dX_s in fp32, rounded once to bf16, written
 //     transposed as G^T [H*d, Kp] (token index b*n + i along K, zero padded
 //     to Kp, a multiple of 64);
-//   * transpose_h_kernel: h^T [D, Kp] bf16;
+//   * transpose_h_kernel: h^T [D, Kp] bf16 (D a multiple of 128);
 //   * gemm_nt_kernel / gemm_nt_256_kernel: dW[M=D, N=H*d] = h^T G (both
 //     operands K-contiguous), bf16 MFMA with fp32 accumulation, a 128x128 or
 //     256x256 output tile per workgroup.
@@ -33,6 +33,9 @@ __device__ inline uint16_t bf16_rne(float v) {
   const uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);   // round to nearest even (finite inputs)
   return (uint16_t)(r >> 16);
 }
+
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+constexpr int kPitch = kTok + 8;   // LDS row pitch of the transpose tiles (16-byte aligned rows)
 
 // One block: 64 tokens x all d components of one head.  Reads dX_s rows
 // (d fp32 each), rotates every pair (k, k + d/2) back, stages bf16 values in
@@ -73,19 +76,24 @@ __global__ __launch_bounds__(256) void rope_t_kernel(const float* dx, const floa
   }
 }
 
-// h [ntok, Dm] bf16 -> h^T [Dm, kp] bf16, 64 x 64 tiles, zero padded along K.
+// h [ntok, Dm] bf16 -> h^T [Dm, kp] bf16 in tiles of 64 tokens x 128 columns,
+// zero padded along K; 16-byte loads (8 columns of a token) and stores (8
+// tokens of a column).
 __global__ __launch_bounds__(256) void transpose_h_kernel(const uint16_t* h, int64_t ntok, int64_t dm, int64_t kp,
                                                           uint16_t* ht) {
-  __shared__ uint16_t tile[64][66];
-  const int64_t tok0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
-    const int t = e / 64, c = e % 64;
-    tile[c][t] = tok0 + t < ntok ? h[(tok0 + t) * dm + c0 + c] : (uint16_t)0;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128][kPitch];
+  const int64_t tok0 = (int64_t)blockIdx.x * kTok, c0 = (int64_t)blockIdx.y * 128;
+  for (int e = threadIdx.x; e < kTok * 16; e += blockDim.x) {
+    const int t = e / 16, c = 8 * (e % 16);
+    u16x8 v = {};
+    if (tok0 + t < ntok) v = *reinterpret_cast<const u16x8*>(h + (tok0 + t) * dm + c0 + c);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) tile[c + q][t] = v[q];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
-    const int c = e / 64, t = e % 64;
-    ht[(c0 + c) * kp + tok0 + t] = tile[c][t];
+  for (int e = threadIdx.x; e < 128 * (kTok / 8); e += blockDim.x) {
+    const int c = e / (kTok / 8), t = 8 * (e % (kTok / 8));
+    *reinterpret_cast<u16x8*>(ht + (c0 + c) * kp + tok0 + t) = *reinterpret_cast<const u16x8*>(&tile[c][t]);
   }
 }
 
@@ -251,7 +259,7 @@ hipError_t launch_proj_bwd(const ProjArgs& p, hipStream_t st) {
   else
     hipLaunchKernelGGL(rope_t_kernel<128>, tgrid, dim3(256), 0, st, p.dx, p.cos, p.sin, p.B, (int)p.n, (int)p.H, p.kp, p.gt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(transpose_h_kernel, dim3((unsigned)(p.kp / 64), (unsigned)(p.dm / 64)), dim3(256), 0, st,
+  hipLaunchKernelGGL(transpose_h_kernel, dim3((unsigned)(p.kp / kTok), (unsigned)(p.dm / 128)), dim3(256), 0, st,
                      p.h, ntok, p.dm, p.kp, p.ht);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return launch_gemm(p.ht, p.gt, p.kp, p.dm, N, p.dw, st);
