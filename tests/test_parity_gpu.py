@@ -78,7 +78,8 @@ def test_tiny_fp32_rope_pi4(gpu_lib):
     _compare(got, ref, "f32", w.n, _logit_bound(m.xt64, m.xs64, w.scale))
 
 
-@pytest.mark.parametrize("n", [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 333])
+# Lengths around the 32-row block, the 128-row tile and the 256-row workgroup.
+@pytest.mark.parametrize("n", [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 333, 511, 513])
 @pytest.mark.parametrize("d", [64, 128])
 def test_bf16_ragged_lengths(gpu_lib, n, d):
     xt, xs = random_pair(1, 2, n, d, 0.4, seed=n * 7 + d)
@@ -100,7 +101,8 @@ def test_fp32_ragged_lengths(gpu_lib, n, d):
     _compare(got, ref, "f32", n, _logit_bound(a, b, s))
 
 
-@pytest.mark.parametrize("n,d,dtype", [(200, 128, "bf16"), (129, 64, "bf16"), (100, 64, "f32")])
+@pytest.mark.parametrize("n,d,dtype", [(200, 128, "bf16"), (129, 64, "bf16"), (100, 64, "f32"), (257, 64, "bf16"),
+                                         (513, 128, "bf16")])
 def test_bidirectional_mask(gpu_lib, n, d, dtype):
     xt, xs = random_pair(1, 3, n, d, 0.5, seed=5, dtype=dtype)
     s = 1.0 / np.sqrt(d)
@@ -196,7 +198,7 @@ def _run_fwd(lmr, xt_np, xs_np, dtype, scale, causal=True):
     return lt.cpu().numpy(), ls.cpu().numpy(), kl.cpu().numpy()
 
 
-@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 129, 200, 333])
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 129, 200, 257, 333, 513])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 def test_kl_fwd_ragged(gpu_lib, n, d, causal):

@@ -26,7 +26,8 @@ def _maps_gqa(B, n, d, Hs, seed, dtype="bf16"):
     return out
 
 
-@pytest.mark.parametrize("n,d,causal", [(200, 128, True), (129, 64, True), (150, 128, False), (1, 128, True)])
+@pytest.mark.parametrize("n,d,causal", [(200, 128, True), (129, 64, True), (150, 128, False), (1, 128, True),
+                                         (300, 128, True)])
 def test_multi_matches_per_map_and_oracle(gpu_lib, n, d, causal):
     import torch
     Hs, weights = (4, 2, 2), (1.0, 0.5, 2.0)

@@ -84,7 +84,7 @@ def _compare(got, ref, dtype, zmax, n, loss_scale=1.0, s=None, ymax=None):
         assert np.array_equal(got[a], got[b]), (a, b)
 
 
-@pytest.mark.parametrize("n", [1, 2, 31, 64, 65, 129, 200, 333])
+@pytest.mark.parametrize("n", [1, 2, 31, 64, 65, 129, 200, 257, 333, 513])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 def test_xy_bf16_ragged(gpu_lib, n, d, causal):
