@@ -12,10 +12,10 @@
 //   * A workgroup of NW waves owns 32*NW consecutive rows of one head; wave w
 //     owns 32 of them.  The owned rows' projections sit in registers as MFMA
 //     B operands for the whole sweep.
-//   * The other index ("swept") advances in tiles of 64 rows that are copied
-//     global -> LDS directly (no staging registers), double-buffered, one
-//     barrier per tile, the copy split over the NW waves.  Each tile is
-//     processed in two 32-row sub-blocks.
+//   * The other index ("swept") advances in tiles of SW rows (128 by
+//     default) that are copied global -> LDS directly (no staging
+//     registers), double-buffered, one barrier per tile, the copy split over
+//     the NW waves.  Each tile is processed in 32-row blocks.
 //   * Logit tiles are computed swept-major: C[swept][owned] =
 //     sum_k X[swept][k] X[owned][k] with v_mfma_f32_32x32x16_bf16, so each
 //     lane holds one owned index and 16 swept indices per 32x32 block.  Row
@@ -322,11 +322,10 @@ __device__ inline WorkItem decode(const MapSet& S, int nblk) {
   return w;
 }
 
-// End of a phase-1 sweep, shared by both sweep schedules: combine the lane
-// pair, store LSE (and row KL), or, if any row of the workgroup overflowed the
-// fixed shift, redo the workgroup's rows with the online maximum.  lds holds
-// at least two double-buffer slots of two tiles; the caller has drained its
-// own tile copies.
+// End of the phase-1 sweep: combine the lane pair, store LSE (and row KL),
+// or, if any row of the workgroup overflowed the fixed shift, redo the
+// workgroup's rows with the online maximum.  lds holds two double-buffer
+// slots of two tiles; every tile copy of the main sweep has completed.
 template <int D, bool KL, int NW, int SW>
 __device__ inline void lse_finish(const SweepArgs& a, int64_t bh, const char* yt, const char* ys,
                                   char (*lds)[2][Tile<D, SW>::BYTES], const bf16x8* Bt, const bf16x8* Bs, int ntiles,
