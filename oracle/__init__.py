@@ -6,5 +6,5 @@ the product path.  See `relation_kl.py` for the definitions and citations.
 """
 from .relation_kl import (  # noqa: F401
     relation_kl_head, relation_kl, relation_kl_xy, lse_rows, row_kl_rows, dx_rows,
-    dx_rows_xy, dy_rows_xy, forward_only_loss, rope_rotate, rope_rotate_transpose, proj_bwd,
+    dx_rows_xy, dy_rows_xy, rope_rotate, rope_rotate_transpose, proj_bwd,
 )

@@ -291,9 +291,3 @@ def proj_bwd(h: np.ndarray, dxs: np.ndarray, cos: Optional[np.ndarray] = None,
     B, H, n, d = g.shape
     gm = np.transpose(g, (0, 2, 1, 3)).reshape(B * n, H * d)
     return h.reshape(B * n, h.shape[-1]).T @ gm
-
-
-def forward_only_loss(xt: np.ndarray, xs: np.ndarray, scale: float,
-                      causal: bool = True) -> float:
-    """Per-head loss only (row mean of KL), via the dense definition."""
-    return relation_kl_head(xt, xs, scale, causal)["loss"]
