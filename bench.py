@@ -41,10 +41,16 @@ def parse():
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="before warm-up, run one fp32 elementwise copy (y = x * 1) of this many MiB; "
                         "its FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
-    p.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "COPY_MIB"),
-                   help="write the markdown summary of rocprofv3 kernel-trace/stats and FETCH_SIZE/WRITE_SIZE "
-                        "runs of this script to stdout and exit")
+    p.add_argument("--summarize", nargs=2, metavar=("TRACE_DIR", "COPY_MIB"),
+                   help="write the markdown summary of a rocprofv3 kernel-trace/stats run of this script and of "
+                        "its --pmc runs (--pmc-dir, one per counter group) to stdout and exit")
+    p.add_argument("--pmc-dir", action="append", default=[],
+                   help="(with --summarize) rocprofv3 -d directory of one --pmc run; repeat per counter group")
     p.add_argument("--trace-cmd", default="", help="(with --summarize) command lines to record in the summary")
+    p.add_argument("--extra-workloads", default="llama2_4k,llama3_gqa_8k,llama2_32k",
+                   help="comma-separated workloads timed after the headline one (same step, fewer steps); "
+                        "empty to skip")
+    p.add_argument("--extra-steps", type=int, default=5)
     p.add_argument("--core-only", action="store_true",
                    help="time only the step (and its one-call check): skip the forward-only, fused-map, "
                         "projection and cross-relation sections, whose launches share kernel symbols with "
@@ -57,8 +63,11 @@ def causal_pairs(n: int) -> int:
 
 
 def cpu_baseline(w, maps, sample_n: int):
-    """Time the fp64 oracle on two head-maps (Q/Q and K/K of b=0, h=0) on the host cores."""
+    """Time the fp64 oracle on two head-maps (Q/Q and K/K of b=0, h=0) on the host cores, and
+    extrapolate it (labelled as such) to the workload's whole step; the tiny fp32 workload is
+    small enough to time in full."""
     import oracle
+    import synth_inputs as si
     try:
         from threadpoolctl import threadpool_info
         cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count() or 1])
@@ -76,11 +85,22 @@ def cpu_baseline(w, maps, sample_n: int):
         assert np.isfinite(r["loss"])
         del r
     flops = len(names) * 12.0 * w.d * causal_pairs(n)
+    step_flops = w.head_maps() * 12.0 * w.d * causal_pairs(w.n)
+    tiny = si.WORKLOADS["tiny_f32"]
+    tq = si.make_inputs(tiny)["Q"]
+    t0 = time.perf_counter()
+    oracle.relation_kl(tq.xt64, tq.xs64, tiny.scale, True)
+    dt_tiny = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": f"{len(names)} head-maps ({', '.join(k + '/' + k for k in names)} of b=0, h=0) of {w.name} "
                       f"at n={n}, d={w.d}: dense fp64 numpy oracle (loss, LSE, row KL, dX_s); "
-                      f"algorithmic flops 12*d*n(n+1)/2 per head-map"}
+                      f"algorithmic flops 12*d*n(n+1)/2 per head-map",
+            "step_seconds_extrapolated": round(dt * step_flops / flops, 1),
+            "extrapolation": f"EXTRAPOLATED: the sample's time scaled by flops to all {w.head_maps()} head-maps "
+                             f"of {w.name} (every head-map of one workload costs the oracle the same)",
+            "tiny_f32_full_step_seconds": round(dt_tiny, 4),
+            "tiny_f32": "the whole tiny_f32 workload (1 head, n=256, d=64), timed, not extrapolated"}
 
 
 # ---------------------------------------------------------------------------
@@ -121,88 +141,160 @@ def _csv_rows(d: str, suffix: str):
     return rows
 
 
-def _pmc_per_dispatch(d: str, counter: str):
-    """Mean of `counter` (KiB) per dispatch, by kernel name."""
+def _pmc_all(dirs):
+    """Per-dispatch counter values from rocprofv3 --pmc runs: {counter: {kernel: [value per dispatch]}}.
+    Rows of one (dispatch, counter) are summed (covers per-dimension rows as well as aggregated ones)."""
     per = {}
-    for r in _csv_rows(d, "counter_collection.csv"):
-        if r.get("Counter_Name") != counter:
-            continue
-        key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id")))
-        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            key = (r["Counter_Name"], r["Kernel_Name"], d, r.get("Dispatch_Id", r.get("Correlation_Id")))
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
     out = {}
-    for (name, _), v in per.items():
-        out.setdefault(name, []).append(v)
-    return {k: (float(np.mean(v)), len(v)) for k, v in out.items()}
+    for (ctr, name, _, _), v in per.items():
+        out.setdefault(ctr, {}).setdefault(name, []).append(v)
+    return out
 
 
-def summarize(trace_dir: str, fetch_dir: str, write_dir: str, copy_mib: str, cmds: str) -> str:
+# Chip constants for AMD's derived utilisation expressions (MfmaUtil, VALUBusy):
+# 256 CUs, 4 SIMDs each, 8 XCDs (GRBM_GUI_ACTIVE is counted once per XCD).
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
+FLOPS_PER_MFMA = 2 * 32 * 32 * 16        # v_mfma_f32_32x32x16_bf16
+ALG_UNITS = {"lse_fwd": 2, "kl_rows": 3, "kl_cols": 1}
+
+
+def summarize(trace_dir: str, copy_mib: str, pmc_dirs, cmds: str) -> str:
+    import linear_memory_relation_amd as lmr
     copy_bytes = int(copy_mib) * 2 ** 20
     stats = _csv_rows(trace_dir, "kernel_stats.csv")
-    fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
-    write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
-    lines = ["# Kernel time and HBM traffic of one relation-KL step (llama2_16k workload)", ""]
+    pmc = _pmc_all(pmc_dirs)
+    lines = ["# Kernel time, hardware counters and HBM traffic of one relation-KL step (llama2_16k workload)", ""]
     lines += ["Workload: B=1, H=32, n=16384, d=128, bf16, maps Q/Q, K/K, V/V, causal, split dX mode.", ""]
-    lines += [f"Library: {__import__('linear_memory_relation_amd').version()}", ""]
+    lines += [f"Library: {lmr.version()}", ""]
     lines += ["Commands (run from the repository root; rocprofv3 wrote CSV under the -d directory):", "", "```"]
     lines += [c for c in cmds.split(";;") if c] + ["```", ""]
     lines += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", ""]
     lines += ["| kernel | kind | calls | avg ms | min ms | max ms | share of GPU time |", "|---|---|---|---|---|---|---|"]
+
     def col(r, *names):
         for k in names:
             for kk in r:
                 if kk.lower().replace("_", "") == k.lower().replace("_", ""):
                     return r[kk]
         raise SystemExit(f"column {names} not in {list(r)}")
+    avg_ns = {}
     for r in sorted(stats, key=lambda r: -float(col(r, "TotalDurationNs"))):
         name = col(r, "Name", "KernelName", "Kernel_Name")
-        lines.append(f"| `{name[:90]}` | {kernel_kind(name)} | {col(r, 'Calls')} | "
+        kind = kernel_kind(name)
+        if kind in ALG_UNITS:
+            avg_ns[kind] = float(col(r, "AverageNs"))
+        lines.append(f"| `{name[:90]}` | {kind} | {col(r, 'Calls')} | "
                      f"{float(col(r, 'AverageNs')) / 1e6:.4f} | {float(col(r, 'MinNs')) / 1e6:.4f} | "
                      f"{float(col(r, 'MaxNs')) / 1e6:.4f} | {float(col(r, 'Percentage')):.2f}% |")
-    cal = [k for k in fetch if kernel_kind(k) == "copy_calibration"]
-    if not cal or not [k for k in write if kernel_kind(k) == "copy_calibration"]:
-        raise SystemExit("calibration copy kernel not found in the counter runs")
-    f_cal = fetch[cal[0]][0] * 1024 / copy_bytes
-    w_cal = write[[k for k in write if kernel_kind(k) == "copy_calibration"][0]][0] * 1024 / copy_bytes
-    lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", ""]
-    lines += [f"Calibration: an fp32 copy of {copy_mib} MiB reads and writes {copy_bytes} bytes; its counters read "
-              f"FETCH_SIZE x {f_cal:.4f} and WRITE_SIZE x {w_cal:.4f} of that, and every figure below is divided "
-              f"by these factors.", ""]
-    lines += ["| kernel | kind | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (calibrated) |",
-              "|---|---|---|---|---|---|"]
-    traffic = {}
-    for name, (fk, cnt) in sorted(fetch.items(), key=lambda kv: -kv[1][0]):
-        wk = write.get(name, (0.0, 0))[0]
-        tb = fk * 1024 / f_cal + wk * 1024 / w_cal
-        kind = kernel_kind(name)
-        if kind in ("lse_fwd", "kl_rows", "kl_cols"):
-            traffic[kind] = tb
-        lines.append(f"| `{name[:90]}` | {kind} | {cnt} | {fk:.1f} | {wk:.1f} | {tb:.4e} |")
-    lines += ["", "Machine-readable (read by bench.py while the kernel sources are unchanged):", ""]
+
+    def by_kind(ctr):
+        """Mean per dispatch of a counter, by kernel kind (sweep kernels only)."""
+        res = {}
+        for name, vals in pmc.get(ctr, {}).items():
+            kind = kernel_kind(name)
+            if kind in ALG_UNITS or kind == "copy_calibration":
+                res.setdefault(kind, []).extend(vals)
+        return {k: float(np.mean(v)) for k, v in res.items()}
+
+    machine = {}
+    # ---- MFMA / VALU utilisation --------------------------------------------
+    gui = by_kind("GRBM_GUI_ACTIVE")
+    busy = by_kind("SQ_VALU_MFMA_BUSY_CYCLES")
+    mops = by_kind("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    nmfma = by_kind("SQ_INSTS_MFMA")
+    valu = by_kind("SQ_ACTIVE_INST_VALU")
+    if gui and busy:
+        import linear_memory_relation_amd  # noqa: F401  (version printed above)
+        from synth_inputs import WORKLOADS
+        w = WORKLOADS["llama2_16k"]
+        unit = 32 * 2 * w.d * causal_pairs(w.n)      # one GEMM-unit over the 32 heads of one map
+        lines += ["", "## MFMA and VALU utilisation (rocprofv3 --pmc, one dispatch at a time)", ""]
+        lines += ["Per sweep kernel, mean over its dispatches (one per map):",
+                  "- `clock` = GRBM_GUI_ACTIVE per XCD / kernel-trace average duration;",
+                  "- `MFMA busy` = sum of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs) "
+                  "(AMD's MfmaUtil expression);",
+                  "- `VALU busy` = sum of SQ_ACTIVE_INST_VALU / 256 CUs / GRBM_GUI_ACTIVE per XCD "
+                  "(AMD's VALUBusy expression);",
+                  "- `executed flop` = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 and, as a cross-check, SQ_INSTS_MFMA x "
+                  f"{FLOPS_PER_MFMA} (one v_mfma_f32_32x32x16_bf16);",
+                  "- `algorithmic flop` = the kernel's share of the method's 6 GEMM-units (phase 1: 2, row sweep: 3, "
+                  "column sweep: 1), one unit = 2*d*n(n+1)/2 flop per head.", ""]
+        lines += ["| kind | clock GHz | MFMA busy | VALU busy | executed flop (MOPS) | executed flop (insts) | "
+                  "algorithmic flop | executed / algorithmic |", "|---|---|---|---|---|---|---|---|"]
+        for kind in ("lse_fwd", "kl_rows", "kl_cols"):
+            if kind not in gui:
+                continue
+            g = gui[kind] / XCD_NUM
+            clk = g / avg_ns[kind] if kind in avg_ns else float("nan")
+            mb = busy.get(kind, float("nan")) / (g * SIMD_NUM)
+            vb = valu.get(kind, float("nan")) / CU_NUM / g
+            ef = mops.get(kind, float("nan")) * 512
+            ei = nmfma.get(kind, float("nan")) * FLOPS_PER_MFMA
+            af = ALG_UNITS[kind] * unit
+            lines.append(f"| {kind} | {clk:.3f} | {mb:.3f} | {vb:.3f} | {ef:.4e} | {ei:.4e} | {af:.4e} | "
+                         f"{ef / af:.3f} |")
+            machine[kind] = {"clock_ghz": clk, "mfma_busy": mb, "valu_busy": vb, "executed_flops": ef,
+                             "executed_over_algorithmic": ef / af}
+    # ---- other SQ counters, raw ---------------------------------------------
+    other = [c for c in sorted(pmc) if c.startswith("SQ_") and c not in (
+        "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU")]
+    if other:
+        lines += ["", "## Further SQ counters (mean per dispatch, summed over the chip)", ""]
+        lines += ["| counter | " + " | ".join(ALG_UNITS) + " |", "|---|" + "---|" * len(ALG_UNITS)]
+        for c in other:
+            v = by_kind(c)
+            lines.append(f"| {c} | " + " | ".join(f"{v[k]:.4e}" if k in v else "-" for k in ALG_UNITS) + " |")
+    # ---- HBM traffic -------------------------------------------------------
+    fetch, write = by_kind("FETCH_SIZE"), by_kind("WRITE_SIZE")
+    if fetch and write:
+        if "copy_calibration" not in fetch or "copy_calibration" not in write:
+            raise SystemExit("calibration copy kernel not found in the FETCH_SIZE / WRITE_SIZE runs")
+        f_cal = fetch["copy_calibration"] * 1024 / copy_bytes
+        w_cal = write["copy_calibration"] * 1024 / copy_bytes
+        lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", ""]
+        lines += [f"Calibration: an fp32 copy of {copy_mib} MiB reads and writes {copy_bytes} bytes; its counters "
+                  f"read FETCH_SIZE x {f_cal:.4f} and WRITE_SIZE x {w_cal:.4f} of that, and every figure below is "
+                  f"divided by these factors.", ""]
+        lines += ["| kind | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (calibrated) |", "|---|---|---|---|"]
+        for kind in ALG_UNITS:
+            if kind not in fetch:
+                continue
+            tb = fetch[kind] * 1024 / f_cal + write.get(kind, 0.0) * 1024 / w_cal
+            machine.setdefault(kind, {})["traffic_bytes_per_launch"] = tb
+            lines.append(f"| {kind} | {fetch[kind]:.1f} | {write.get(kind, 0.0):.1f} | {tb:.4e} |")
+    lines += ["", "Machine-readable (read by bench.py while the library sources are unchanged):", ""]
     lines.append(f"library_source_id: {library_source_id()}")
-    for k, v in sorted(traffic.items()):
-        lines.append(f"traffic_bytes_per_launch {k}: {v:.6e}")
+    for kind, vals in sorted(machine.items()):
+        for k, v in sorted(vals.items()):
+            lines.append(f"counter {kind} {k}: {v:.6e}")
     return "\n".join(lines) + "\n"
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kernel_trace_and_traffic_llama2_16k.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "sweep_kernels_llama2_16k.md")
 
 
-def recorded_traffic(kind: str, workload: str):
-    """Calibrated HBM bytes per launch of `kind` from the committed summary, or None when the
-    summary is missing, covers another workload or was taken on a library built from other sources."""
+def recorded_counters(kind: str, workload: str):
+    """Counter-derived figures of `kind` (traffic, MFMA/VALU busy, executed flops) from the committed
+    summary, or {} when the summary is missing, covers another workload or was taken on a library
+    built from other sources."""
     import linear_memory_relation_amd as lmr
     if workload != "llama2_16k" or not os.path.exists(TRAFFIC_SUMMARY):
-        return None
-    src, val = None, None
+        return {}
+    src, vals = None, {}
     with open(TRAFFIC_SUMMARY) as f:
         for line in f:
             if line.startswith("library_source_id:"):
                 src = line.split(":", 1)[1].strip()
-            if line.startswith(f"traffic_bytes_per_launch {kind}:"):
-                val = float(line.split(":", 1)[1])
+            if line.startswith(f"counter {kind} "):
+                key, val = line[len(f"counter {kind} "):].split(":", 1)
+                vals[key.strip()] = float(val)
     if src != lmr.source_id():
-        return None
-    return val
+        return {}
+    return vals
 
 
 def extra_sections(args, bufs, w, scale, dev, units, step_flops):
@@ -325,10 +417,133 @@ def extra_sections(args, bufs, w, scale, dev, units, step_flops):
     return fwd_info, proj, cross, fused_info
 
 
+def make_buffers(w, dev):
+    """Device inputs and outputs of every map of workload `w` (inputs resident in HBM)."""
+    import torch
+    import synth_inputs as si
+    maps = si.make_inputs(w)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    bufs = []
+    for name, m in maps.items():
+        B, H, n, d = m.xt.shape
+        bufs.append(dict(
+            name=name, B=B, H=H, n=n, d=d, xt=to_dev(m.xt), xs=to_dev(m.xs),
+            lse_t=torch.empty((B, H, n), dtype=torch.float64, device=dev),
+            lse_s=torch.empty((B, H, n), dtype=torch.float64, device=dev),
+            row_kl=torch.empty((B, H, n), dtype=torch.float32, device=dev),
+            partials=torch.empty((B * H,), dtype=torch.float64, device=dev),
+            dx=torch.empty((B, H, n, d), dtype=torch.float32, device=dev),
+            loss=torch.empty((), dtype=torch.float32, device=dev)))
+    return maps, bufs
+
+
+KINDS = ["lse_fwd", "kl_rows", "kl_cols", "reduce"]
+
+
+def run_steps(bufs, scale, steps, warmup, events=True):
+    """Warm up, then time `steps` steps (each map: phase 1, row sweep, column sweep, reduction,
+    as larard_loss launches them) with HIP events on the launch stream.  Returns
+    (ms per step, per-kernel times in ms, wall seconds of the timed region)."""
+    import torch
+    import linear_memory_relation_amd as lmr
+
+    def step(ev=None):
+        for b in bufs:
+            a = (b["xt"], b["xs"])
+            if ev is not None:
+                ev[b["name"]][0].record()
+            lmr.lse_fwd(*a, scale, True, b["lse_t"], b["lse_s"])
+            if ev is not None:
+                ev[b["name"]][1].record()
+            lmr.kl_bwd_rows(*a, b["lse_t"], b["lse_s"], b["row_kl"], b["dx"], scale, True, 1.0)
+            if ev is not None:
+                ev[b["name"]][2].record()
+            lmr.kl_bwd_cols(*a, b["lse_t"], b["lse_s"], b["dx"], scale, True, 1.0)
+            if ev is not None:
+                ev[b["name"]][3].record()
+            lmr.reduce_loss(b["row_kl"], b["partials"], b["loss"], 1.0)
+            if ev is not None:
+                ev[b["name"]][4].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [{b["name"]: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for b in bufs}
+          for _ in range(steps)] if events else [None] * steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for k in range(steps):
+        step(ev[k])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    per_kernel = {k: [] for k in KINDS}
+    if events:
+        for k in range(steps):
+            for b in bufs:
+                e = ev[k][b["name"]]
+                for j, kind in enumerate(KINDS):
+                    per_kernel[kind].append(e[j].elapsed_time(e[j + 1]))
+    return total_ms / steps, per_kernel, total_ms, wall
+
+
+def units(b):
+    """One GEMM-unit of a map: 2*d flop per kept pair, over all its heads."""
+    return b["B"] * b["H"] * 2 * b["d"] * causal_pairs(b["n"])
+
+
+def memory_report(bufs, base_alloc, peak_alloc, free_before, free_after_alloc, free_after_steps):
+    inputs = sum(b["xt"].numel() * 2 * 2 for b in bufs)
+    dx = sum(b["dx"].numel() * 4 for b in bufs)
+    stats = sum(b["lse_t"].numel() * (8 + 8 + 4) + b["partials"].numel() * 8 for b in bufs)
+    return {"peak_alloc_bytes_during_steps": int(peak_alloc),
+            "hip_mem_used_by_buffers_bytes": int(free_before - free_after_alloc),
+            "hip_mem_growth_during_steps_bytes": int(free_after_alloc - free_after_steps),
+            "inputs_bytes": inputs, "dx_bytes": dx, "statistics_bytes": stats,
+            "extra_beyond_inputs_and_dx_bytes": int(peak_alloc - inputs - dx),
+            "bhn_bound_bytes": int(sum(20 * b["B"] * b["H"] * b["n"] + 8 * b["B"] * b["H"] for b in bufs)),
+            "dense_fp32_map_bytes_one_matrix": int(sum(4 * b["B"] * b["H"] * b["n"] ** 2 for b in bufs))}
+
+
+def extra_workload(name, args, dev):
+    """ms/step, TFLOP/s and memory of one more workload, timed like the headline one."""
+    import gc
+    import torch
+    import synth_inputs as si
+    w = si.WORKLOADS[name]
+    torch.cuda.synchronize()
+    free_before = torch.cuda.mem_get_info()[0]
+    base_alloc = torch.cuda.memory_allocated()
+    maps, bufs = make_buffers(w, dev)
+    del maps
+    torch.cuda.synchronize()
+    free_after_alloc = torch.cuda.mem_get_info()[0]
+    torch.cuda.reset_peak_memory_stats()
+    ms, per_kernel, _, _ = run_steps(bufs, w.scale, args.extra_steps, 1)
+    free_after_steps = torch.cuda.mem_get_info()[0]
+    peak = torch.cuda.max_memory_allocated() - base_alloc
+    flops = sum(6 * units(b) for b in bufs)
+    out = {"workload": name, "B": w.B, "n": w.n, "d": w.d, "heads": w.heads, "steps": args.extra_steps,
+           "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+           "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "kernels_avg_ms": {k: round(float(np.mean(v)), 4) for k, v in per_kernel.items()},
+           "losses": {b["name"]: float(b["loss"].cpu()) for b in bufs},
+           "memory": memory_report(bufs, base_alloc, peak, free_before, free_after_alloc, free_after_steps)}
+    del bufs
+    gc.collect()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.summarize:
-        sys.stdout.write(summarize(*args.summarize, args.trace_cmd))
+        sys.stdout.write(summarize(args.summarize[0], args.summarize[1], args.pmc_dir, args.trace_cmd))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this kernel shards by heads "
@@ -346,83 +561,30 @@ def main():
     lmr.load()
     dev = torch.device("cuda:0")
     w = si.WORKLOADS[args.workload]
-    maps = si.make_inputs(w)
     scale = w.scale
 
-    def to_dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
     torch.cuda.synchronize()
+    free_before = torch.cuda.mem_get_info()[0]
     base_alloc = torch.cuda.memory_allocated()
-    bufs = []
-    for name, m in maps.items():
-        B, H, n, d = m.xt.shape
-        bufs.append(dict(
-            name=name, B=B, H=H, n=n, d=d, xt=to_dev(m.xt), xs=to_dev(m.xs),
-            lse_t=torch.empty((B, H, n), dtype=torch.float64, device=dev),
-            lse_s=torch.empty((B, H, n), dtype=torch.float64, device=dev),
-            row_kl=torch.empty((B, H, n), dtype=torch.float32, device=dev),
-            partials=torch.empty((B * H,), dtype=torch.float64, device=dev),
-            dx=torch.empty((B, H, n, d), dtype=torch.float32, device=dev),
-            loss=torch.empty((), dtype=torch.float32, device=dev)))
-    input_bytes = sum(b["xt"].numel() * 2 * 2 for b in bufs)
-    dx_bytes = sum(b["dx"].numel() * 4 for b in bufs)
-    stat_bytes = sum(b["lse_t"].numel() * (8 + 8 + 4) + b["partials"].numel() * 8 for b in bufs)
+    maps, bufs = make_buffers(w, dev)
     torch.cuda.synchronize()
+    free_after_alloc = torch.cuda.mem_get_info()[0]
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib * 2 ** 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
+        torch.cuda.empty_cache()
+        free_after_alloc = torch.cuda.mem_get_info()[0]
     torch.cuda.reset_peak_memory_stats()
-
-    kinds = ["lse_fwd", "kl_rows", "kl_cols", "reduce"]
-
-    def step(events=None):
-        for b in bufs:
-            a = (b["xt"], b["xs"])
-            if events is not None:
-                events[b["name"]][0].record()
-            lmr.lse_fwd(*a, scale, True, b["lse_t"], b["lse_s"])
-            if events is not None:
-                events[b["name"]][1].record()
-            lmr.kl_bwd_rows(*a, b["lse_t"], b["lse_s"], b["row_kl"], b["dx"], scale, True, 1.0)
-            if events is not None:
-                events[b["name"]][2].record()
-            lmr.kl_bwd_cols(*a, b["lse_t"], b["lse_s"], b["dx"], scale, True, 1.0)
-            if events is not None:
-                events[b["name"]][3].record()
-            lmr.reduce_loss(b["row_kl"], b["partials"], b["loss"], 1.0)
-            if events is not None:
-                events[b["name"]][4].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
 
     # Timed region: K steps with HIP events around every kernel, on the stream
     # the kernels are launched on (torch's current stream).
-    ev = [{b["name"]: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for b in bufs}
-          for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record()
-    for k in range(args.steps):
-        step(ev[k])
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
-    per_kernel = {k: [] for k in kinds}
-    for k in range(args.steps):
-        for b in bufs:
-            e = ev[k][b["name"]]
-            for j, kind in enumerate(kinds):
-                per_kernel[kind].append(e[j].elapsed_time(e[j + 1]))
+    ms_step, per_kernel, total_ms, wall = run_steps(bufs, scale, args.steps, args.warmup)
+    free_after_steps = torch.cuda.mem_get_info()[0]
     peak_alloc = torch.cuda.max_memory_allocated() - base_alloc
+    memory = memory_report(bufs, base_alloc, peak_alloc, free_before, free_after_alloc, free_after_steps)
 
     # Independent check of the one-call path: same kernels, no events.
     torch.cuda.synchronize()
@@ -436,9 +598,8 @@ def main():
     torch.cuda.synchronize()
     ms_step_oneshot = s2.elapsed_time(e2) / args.steps
     losses = {b["name"]: float(b["loss"].cpu()) for b in bufs}
+    del ws
 
-    def units(b):
-        return b["B"] * b["H"] * 2 * b["d"] * causal_pairs(b["n"])
     step_flops = sum(6 * units(b) for b in bufs)
 
     fwd_info, proj, cross, fused_info = None, None, None, None
@@ -453,27 +614,39 @@ def main():
     alg = {"lse_fwd": 2, "kl_rows": 3, "kl_cols": 1, "reduce": 0}
     exe = {"lse_fwd": 2, "kl_rows": 3, "kl_cols": 3, "reduce": 0}
     kern = {}
-    for kind in kinds:
+    for kind in KINDS:
         t = float(np.mean(per_kernel[kind]))
         fl = np.mean([alg[kind] * units(b) for b in bufs])
         fe = np.mean([exe[kind] * units(b) for b in bufs])
         kern[kind] = {"avg_ms": t, "share": float(np.sum(per_kernel[kind]) / total_ms),
                       "alg_tflops": fl / (t * 1e-3) / 1e12 if fl else 0.0,
                       "executed_tflops": fe / (t * 1e-3) / 1e12 if fe else 0.0}
+
     # Roofline of every sweep kernel; `roofline` is the one with the largest
-    # share of the step's time (the row and column sweeps are close, so the
-    # choice can differ between runs).
+    # share of the step's time.  Counter-derived figures (HBM traffic, MFMA and
+    # VALU busy fractions, executed flops) come from the committed rocprofv3
+    # summary when it was taken on a library built from the same sources.
     def roof(kind):
         fl = float(np.mean([alg[kind] * units(b) for b in bufs]))
         ach = fl / (kern[kind]["avg_ms"] * 1e-3) / 1e12
+        ctr = recorded_counters(kind, w.name)
         return {"kernel": kind, "bound": "mfma", "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(kind, w.name),
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": ctr.get("traffic_bytes_per_launch"),
                 "alg_flops_per_launch": fl,
                 "executed_frac": round(kern[kind]["executed_tflops"] / PEAK_BF16_TFLOPS, 4),
+                "counters": {k: ctr[k] for k in ("mfma_busy", "valu_busy", "clock_ghz", "executed_flops",
+                                                 "executed_over_algorithmic") if k in ctr} or None,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"}
-    sweeps = [k for k in kinds if alg[k] > 0]
-    dom = max(kinds, key=lambda k: kern[k]["share"])
+    sweeps = [k for k in KINDS if alg[k] > 0]
+    dom = max(KINDS, key=lambda k: kern[k]["share"])
     value = step_flops / (ms_step * 1e-3) / 1e12
+
+    extra = {}
+    del bufs
+    torch.cuda.empty_cache()
+    for name in [x for x in args.extra_workloads.split(",") if x and x != w.name]:
+        extra[name] = extra_workload(name, args, dev)
 
     out = {
         "metric": "relation-KL fwd+bwd ms/step & TFLOP/s (% bf16 MFMA peak) at H=32,d=128,n=16K",
@@ -496,11 +669,9 @@ def main():
         "kernels": kern,
         "ms_per_step_one_call": round(ms_step_oneshot, 4),
         "wall_s_timed": round(wall, 3),
-        "memory": {"peak_alloc_bytes_during_steps": int(peak_alloc), "inputs_bytes": input_bytes,
-                   "dx_bytes": dx_bytes, "statistics_bytes": stat_bytes,
-                   "bhn_bound_bytes": int(sum(20 * b["B"] * b["H"] * b["n"] for b in bufs)),
-                   "dense_fp32_map_bytes_one_matrix": int(sum(4 * b["B"] * b["H"] * b["n"] ** 2 for b in bufs))},
+        "memory": memory,
         "losses": losses,
+        "other_workloads": extra,
         "forward_only": fwd_info,
         "cross_relation": cross,
         "proj_bwd": proj,

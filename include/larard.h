@@ -62,10 +62,14 @@ typedef enum { LARARD_BF16 = 0, LARARD_FP32 = 1 } larard_dtype;
 
 /* How phase 2 produces the column term dZ^T X_s of the gradient.
  *   SPLIT : a second, column-owned sweep recomputes the logit tiles and adds
- *           the column term; deterministic, no atomics.
- *   ATOMIC: the row-owned sweep adds the column term with fp32 atomics;
- *           one sweep, last-bit run-to-run variation.
- *   AUTO  : the mode measured fastest for the shape. */
+ *           the column term; deterministic, no atomics.  The only mode built.
+ *   ATOMIC: not built; every call that passes it returns
+ *           LARARD_E_UNSUPPORTED.  (A row sweep that adds its column partials
+ *           with fp32 atomics must add B*H*n^2 bytes per map with 256-row
+ *           workgroups -- 8.6 GB at n = 16K, H = 32 -- and coalesced fp32
+ *           atomic adds sustain ~1.4 TB/s on MI355X, longer than the
+ *           split's whole second sweep.)
+ *   AUTO  : SPLIT. */
 typedef enum { LARARD_DX_AUTO = 0, LARARD_DX_SPLIT = 1, LARARD_DX_ATOMIC = 2 } larard_dx_mode;
 
 /* Bytes of workspace larard_loss needs: LSE_t and LSE_s (B*H*n fp64 each),
@@ -76,9 +80,13 @@ typedef enum { LARARD_DX_AUTO = 0, LARARD_DX_SPLIT = 1, LARARD_DX_ATOMIC = 2 } l
 size_t larard_workspace_bytes(larard_dtype dtype, int64_t B, int64_t H, int64_t n);
 
 /* Phase 1 (notes page, "Key designs" item 3; summary page, "Method"):
- * streams key tiles with an online max/sum and writes
+ * streams key tiles and writes
  *   lse_t[b,h,i] = log sum_{j kept} exp(scale * <x_t,i , x_t,j>)
- * and likewise lse_s, fp64 [B, H, n].  No other output. */
+ * and likewise lse_s, fp64 [B, H, n].  No other output.  Each row's sum is
+ * taken against a fixed shift, the row's own diagonal logit (always a kept
+ * entry), instead of a running maximum; if any row of a 256-row block
+ * overflows or underflows that shift, the block redoes its rows with an
+ * online maximum.  The result is the same exact LSE either way. */
 larard_status larard_lse_fwd(const void* x_t, const void* x_s, larard_dtype dtype,
                              int64_t B, int64_t H, int64_t n, int64_t d,
                              float scale, int causal,
@@ -203,8 +211,10 @@ larard_status larard_xy_loss(const void* x_t, const void* x_s, const void* y_t, 
  * weighted sum of the Q/Q, K/K and V/V map losses, weights lambda = 1 in the
  * pages).  Maps share B, n, d, dtype, scale and causal; each has its own head
  * count (GQA: 32 query heads, 8 key/value heads) and weight.  Every kernel
- * runs once over the heads of all maps, longest row blocks of every map
- * first, so small maps fill the tail of large ones.
+ * runs once over the heads of all maps, saving the launch gaps and the
+ * drained tail between per-map launches.  Work is ordered map by map (map 0
+ * first), and within a map by row-block length (longest first) and then by
+ * head.
  * ------------------------------------------------------------------------- */
 typedef struct {
   const void* x_t;   /* [B, H, n, d] teacher projections of this map (device) */

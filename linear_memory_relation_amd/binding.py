@@ -109,11 +109,53 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _shape(xt: torch.Tensor, xs: torch.Tensor):
+    """(B, H, n, d) of a teacher/student pair; shape, dtype and layout only (the device is
+    checked by _on_gpu once every buffer of the call has been checked)."""
+    if not (isinstance(xt, torch.Tensor) and isinstance(xs, torch.Tensor)):
+        raise ValueError("x_t and x_s must be torch tensors")
     if xt.dim() != 4 or xt.shape != xs.shape or xt.dtype != xs.dtype:
         raise ValueError("x_t and x_s must both be [B, H, n, d] with the same dtype")
-    if not (xt.is_cuda and xs.is_cuda and xt.is_contiguous() and xs.is_contiguous()):
-        raise ValueError("x_t and x_s must be contiguous GPU tensors")
+    _dtype_code(xt)
+    if not (xt.is_contiguous() and xs.is_contiguous()):
+        raise ValueError("x_t and x_s must be contiguous")
     return tuple(int(v) for v in xt.shape)
+
+
+def _need(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype, optional: bool = False) -> None:
+    """A caller-supplied buffer must be a contiguous tensor of exactly this shape and dtype
+    (the kernels index it by the shape of the inputs, so anything else reads or writes out of
+    bounds)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_bytes(t: Optional[torch.Tensor], name: str, nbytes: int) -> None:
+    """A caller-supplied workspace: any contiguous tensor of at least nbytes bytes."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} must hold at least {nbytes} bytes, got {t.numel() * t.element_size()}")
+
+
+def _on_gpu(*tensors: Optional[torch.Tensor]) -> None:
+    """Every tensor of one call must live on the same GPU."""
+    ts = [t for t in tensors if t is not None]
+    if not all(t.is_cuda for t in ts):
+        raise ValueError("every tensor of the call must be a GPU tensor")
+    if len({t.device for t in ts}) > 1:
+        raise ValueError("every tensor of the call must be on the same GPU")
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -149,6 +191,9 @@ def lse_fwd(xt: torch.Tensor, xs: torch.Tensor, scale: Optional[float] = None, c
     """Phase 1: per-row log-sum-exp of teacher and student logits, fp64 [B, H, n]."""
     B, H, n, d = _shape(xt, xs)
     scale = default_scale(d) if scale is None else float(scale)
+    _need(lse_t, "lse_t", (B, H, n), torch.float64, optional=True)
+    _need(lse_s, "lse_s", (B, H, n), torch.float64, optional=True)
+    _on_gpu(xt, xs, lse_t, lse_s)
     if lse_t is None:
         lse_t = torch.empty((B, H, n), dtype=stat_dtype(xt), device=xt.device)
     if lse_s is None:
@@ -165,6 +210,10 @@ def kl_fwd(xt: torch.Tensor, xs: torch.Tensor, scale: Optional[float] = None, ca
     """Forward-only sweep: (lse_t, lse_s, row_kl) -- fp64, fp64, fp32 [B, H, n] -- in one pass."""
     B, H, n, d = _shape(xt, xs)
     scale = default_scale(d) if scale is None else float(scale)
+    _need(lse_t, "lse_t", (B, H, n), torch.float64, optional=True)
+    _need(lse_s, "lse_s", (B, H, n), torch.float64, optional=True)
+    _need(row_kl, "row_kl", (B, H, n), torch.float32, optional=True)
+    _on_gpu(xt, xs, lse_t, lse_s, row_kl)
     if lse_t is None:
         lse_t = torch.empty((B, H, n), dtype=stat_dtype(xt), device=xt.device)
     if lse_s is None:
@@ -184,12 +233,17 @@ def kl_bwd(xt: torch.Tensor, xs: torch.Tensor, lse_t: torch.Tensor, lse_s: torch
     """Phase 2: per-row KL(R_t || R_s) (fp32 [B,H,n]) and dX_s (fp32 [B,H,n,d] or None)."""
     B, H, n, d = _shape(xt, xs)
     scale = default_scale(d) if scale is None else float(scale)
+    if not need_dx:
+        dx = None
+    _need(lse_t, "lse_t", (B, H, n), torch.float64)
+    _need(lse_s, "lse_s", (B, H, n), torch.float64)
+    _need(row_kl, "row_kl", (B, H, n), torch.float32, optional=True)
+    _need(dx, "dx", (B, H, n, d), torch.float32, optional=True)
+    _on_gpu(xt, xs, lse_t, lse_s, row_kl, dx)
     if row_kl is None:
         row_kl = torch.empty((B, H, n), dtype=torch.float32, device=xt.device)
     if need_dx and dx is None:
         dx = torch.empty((B, H, n, d), dtype=torch.float32, device=xt.device)
-    if not need_dx:
-        dx = None
     st = load().larard_kl_bwd(_ptr(xt), _ptr(xs), _dtype_code(xt), B, H, n, d, scale, int(causal),
                               _ptr(lse_t), _ptr(lse_s), float(loss_scale), _ptr(row_kl), _ptr(dx),
                               int(dx_mode), _stream())
@@ -201,6 +255,11 @@ def kl_bwd_rows(xt, xs, lse_t, lse_s, row_kl, dx=None, scale=None, causal=True, 
     """Row-owned half of phase 2: writes row_kl, stores the row term into dx (if given)."""
     B, H, n, d = _shape(xt, xs)
     scale = default_scale(d) if scale is None else float(scale)
+    _need(lse_t, "lse_t", (B, H, n), torch.float64)
+    _need(lse_s, "lse_s", (B, H, n), torch.float64)
+    _need(row_kl, "row_kl", (B, H, n), torch.float32)
+    _need(dx, "dx", (B, H, n, d), torch.float32, optional=True)
+    _on_gpu(xt, xs, lse_t, lse_s, row_kl, dx)
     st = load().larard_kl_bwd_rows(_ptr(xt), _ptr(xs), _dtype_code(xt), B, H, n, d, scale, int(causal),
                                    _ptr(lse_t), _ptr(lse_s), float(loss_scale), _ptr(row_kl), _ptr(dx),
                                    _stream())
@@ -211,6 +270,10 @@ def kl_bwd_cols(xt, xs, lse_t, lse_s, dx, scale=None, causal=True, loss_scale=1.
     """Column-owned half of phase 2: adds the column term into dx."""
     B, H, n, d = _shape(xt, xs)
     scale = default_scale(d) if scale is None else float(scale)
+    _need(lse_t, "lse_t", (B, H, n), torch.float64)
+    _need(lse_s, "lse_s", (B, H, n), torch.float64)
+    _need(dx, "dx", (B, H, n, d), torch.float32)
+    _on_gpu(xt, xs, lse_t, lse_s, dx)
     st = load().larard_kl_bwd_cols(_ptr(xt), _ptr(xs), _dtype_code(xt), B, H, n, d, scale, int(causal),
                                    _ptr(lse_t), _ptr(lse_s), float(loss_scale), _ptr(dx), _stream())
     _check(st, "larard_kl_bwd_cols")
@@ -218,7 +281,13 @@ def kl_bwd_cols(xt, xs, lse_t, lse_s, dx, scale=None, causal=True, loss_scale=1.
 
 def reduce_loss(row_kl: torch.Tensor, partials: torch.Tensor, out: torch.Tensor, loss_scale: float = 1.0):
     """loss = loss_scale * sum over heads of the row mean of row_kl ([B, H, n] fp32)."""
+    if not isinstance(row_kl, torch.Tensor) or row_kl.dim() != 3:
+        raise ValueError("row_kl must be a [B, H, n] tensor")
     B, H, n = (int(v) for v in row_kl.shape)
+    _need(row_kl, "row_kl", (B, H, n), torch.float32)
+    _need(partials, "partials", (B * H,), torch.float64)
+    _need(out, "out", (), torch.float32)
+    _on_gpu(row_kl, partials, out)
     st = load().larard_reduce_loss(_ptr(row_kl), B, H, n, float(loss_scale), _ptr(partials), _ptr(out),
                                    _stream())
     _check(st, "larard_reduce_loss")
@@ -232,14 +301,18 @@ def loss(xt: torch.Tensor, xs: torch.Tensor, scale: Optional[float] = None, caus
     B, H, n, d = _shape(xt, xs)
     scale = default_scale(d) if scale is None else float(scale)
     nbytes = workspace_bytes(B, H, n, _dtype_code(xt))
+    if not need_dx:
+        dx = None
+    _need_bytes(workspace, "workspace", nbytes)
+    _need(out, "out", (), torch.float32, optional=True)
+    _need(dx, "dx", (B, H, n, d), torch.float32, optional=True)
+    _on_gpu(xt, xs, workspace, out, dx)
     if workspace is None:
         workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=xt.device)
     if out is None:
         out = torch.empty((), dtype=torch.float32, device=xt.device)
     if need_dx and dx is None:
         dx = torch.empty((B, H, n, d), dtype=torch.float32, device=xt.device)
-    if not need_dx:
-        dx = None
     st = load().larard_loss(_ptr(xt), _ptr(xs), _dtype_code(xt), B, H, n, d, scale, int(causal),
                             float(loss_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
                             _ptr(out), _ptr(dx), int(dx_mode), _stream())
@@ -257,10 +330,18 @@ def _shape_xy(xt, xs, yt, ys):
     return shp
 
 
+def _xy_stats(B, H, n, lse_t, lse_s, row_kl, required: bool):
+    _need(lse_t, "lse_t", (B, H, n), torch.float64, optional=not required)
+    _need(lse_s, "lse_s", (B, H, n), torch.float64, optional=not required)
+    _need(row_kl, "row_kl", (B, H, n), torch.float32, optional=True)
+
+
 def xy_lse_fwd(xt, xs, yt, ys, scale=None, causal=True, lse_t=None, lse_s=None):
     """Phase 1 of the X/Y relation: (lse_t, lse_s), fp64 [B, H, n]."""
     B, H, n, d = _shape_xy(xt, xs, yt, ys)
     scale = default_scale(d) if scale is None else float(scale)
+    _xy_stats(B, H, n, lse_t, lse_s, None, False)
+    _on_gpu(xt, xs, yt, ys, lse_t, lse_s)
     lse_t = torch.empty((B, H, n), dtype=torch.float64, device=xt.device) if lse_t is None else lse_t
     lse_s = torch.empty((B, H, n), dtype=torch.float64, device=xt.device) if lse_s is None else lse_s
     st = load().larard_xy_lse_fwd(_ptr(xt), _ptr(xs), _ptr(yt), _ptr(ys), _dtype_code(xt), B, H, n, d, scale,
@@ -273,6 +354,8 @@ def xy_kl_fwd(xt, xs, yt, ys, scale=None, causal=True, lse_t=None, lse_s=None, r
     """Forward-only X/Y relation in one sweep: (lse_t, lse_s, row_kl)."""
     B, H, n, d = _shape_xy(xt, xs, yt, ys)
     scale = default_scale(d) if scale is None else float(scale)
+    _xy_stats(B, H, n, lse_t, lse_s, row_kl, False)
+    _on_gpu(xt, xs, yt, ys, lse_t, lse_s, row_kl)
     lse_t = torch.empty((B, H, n), dtype=torch.float64, device=xt.device) if lse_t is None else lse_t
     lse_s = torch.empty((B, H, n), dtype=torch.float64, device=xt.device) if lse_s is None else lse_s
     row_kl = torch.empty((B, H, n), dtype=torch.float32, device=xt.device) if row_kl is None else row_kl
@@ -287,6 +370,12 @@ def xy_kl_bwd(xt, xs, yt, ys, lse_t, lse_s, scale=None, causal=True, loss_scale=
     """Phase 2 of the X/Y relation: (row_kl, dX_s or None, dY_s or None)."""
     B, H, n, d = _shape_xy(xt, xs, yt, ys)
     scale = default_scale(d) if scale is None else float(scale)
+    dx = dx if need_dx else None
+    dy = dy if need_dy else None
+    _xy_stats(B, H, n, lse_t, lse_s, row_kl, True)
+    _need(dx, "dx", (B, H, n, d), torch.float32, optional=True)
+    _need(dy, "dy", (B, H, n, d), torch.float32, optional=True)
+    _on_gpu(xt, xs, yt, ys, lse_t, lse_s, row_kl, dx, dy)
     row_kl = torch.empty((B, H, n), dtype=torch.float32, device=xt.device) if row_kl is None else row_kl
     dx = (torch.empty((B, H, n, d), dtype=torch.float32, device=xt.device) if dx is None else dx) if need_dx else None
     dy = (torch.empty((B, H, n, d), dtype=torch.float32, device=xt.device) if dy is None else dy) if need_dy else None
@@ -303,6 +392,13 @@ def xy_loss(xt, xs, yt, ys, scale=None, causal=True, loss_scale=1.0, need_grad=T
     B, H, n, d = _shape_xy(xt, xs, yt, ys)
     scale = default_scale(d) if scale is None else float(scale)
     nbytes = workspace_bytes(B, H, n, _dtype_code(xt))
+    if not need_grad:
+        dx = dy = None
+    _need_bytes(workspace, "workspace", nbytes)
+    _need(out, "out", (), torch.float32, optional=True)
+    _need(dx, "dx", (B, H, n, d), torch.float32, optional=True)
+    _need(dy, "dy", (B, H, n, d), torch.float32, optional=True)
+    _on_gpu(xt, xs, yt, ys, workspace, out, dx, dy)
     if workspace is None:
         workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=xt.device)
     out = torch.empty((), dtype=torch.float32, device=xt.device) if out is None else out
@@ -344,16 +440,23 @@ def multi_loss(maps, scale: Optional[float] = None, causal: bool = True, loss_sc
     receives that map's gradient, or None for every map (loss only).
     Returns the loss as a 0-d fp32 device tensor.
     """
+    if not maps:
+        raise ValueError("maps must not be empty")
     xt0 = maps[0][0]
+    _shape(xt0, maps[0][1])
     B, _, n, d = (int(v) for v in xt0.shape)
-    for xt, xs, _, dx in maps:
-        _shape(xt, xs)
+    for k, (xt, xs, _, dx) in enumerate(maps):
+        _, Hm, _, _ = _shape(xt, xs)
         if xt.shape[0] != B or xt.shape[2] != n or xt.shape[3] != d or xt.dtype != xt0.dtype:
             raise ValueError("maps must share B, n, d and dtype")
+        _need(dx, f"dx of map {k}", (B, Hm, n, d), torch.float32, optional=True)
     scale = default_scale(d) if scale is None else float(scale)
     arr = _map_array(maps)
     code = _dtype_code(xt0)
     nbytes = int(load().larard_multi_workspace_bytes(code, B, n, arr, len(maps)))
+    _need_bytes(workspace, "workspace", nbytes)
+    _need(out, "out", (), torch.float32, optional=True)
+    _on_gpu(*[t for xt, xs, _, dx in maps for t in (xt, xs, dx)], workspace, out)
     if workspace is None:
         workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=xt0.device)
     out = torch.empty((), dtype=torch.float32, device=xt0.device) if out is None else out
@@ -372,13 +475,23 @@ def proj_bwd(h: torch.Tensor, dx_s: torch.Tensor, rope_cos: Optional[torch.Tenso
              out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """h: bf16 [B, n, dm]; dx_s: fp32 [B, H, n, d]; rope tables fp32 [n, d/2] or None.
     Returns dW fp32 [dm, H*d]."""
+    if not (isinstance(h, torch.Tensor) and isinstance(dx_s, torch.Tensor)) or h.dim() != 3 or dx_s.dim() != 4:
+        raise ValueError("h must be bf16 [B, n, dm] and dx_s fp32 [B, H, n, d]")
     B, n, dm = (int(v) for v in h.shape)
     _, H, n2, d = (int(v) for v in dx_s.shape)
     if n2 != n or dx_s.shape[0] != B or h.dtype != torch.bfloat16 or dx_s.dtype != torch.float32:
         raise ValueError("h must be bf16 [B, n, dm] and dx_s fp32 [B, H, n, d]")
     if not (h.is_contiguous() and dx_s.is_contiguous()):
         raise ValueError("h and dx_s must be contiguous")
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("rope_cos and rope_sin must both be given or both be None")
+    # Half-width tables: entry [i, k] turns the pair (k, k + d/2) of token i.
+    _need(rope_cos, "rope_cos", (n, d // 2), torch.float32, optional=True)
+    _need(rope_sin, "rope_sin", (n, d // 2), torch.float32, optional=True)
+    _need(out, "out", (dm, H * d), torch.float32, optional=True)
     nbytes = int(load().larard_proj_bwd_workspace_bytes(B, n, dm, H, d))
+    _need_bytes(workspace, "workspace", nbytes)
+    _on_gpu(h, dx_s, rope_cos, rope_sin, workspace, out)
     if workspace is None:
         workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=h.device)
     out = torch.empty((dm, H * d), dtype=torch.float32, device=h.device) if out is None else out

@@ -1,10 +1,18 @@
 """GPU parity of the projection backward dW = h^T R^T(dX_s) against the fp64 oracle.
 
 The kernel rounds G = R^T dX_s (computed in fp32) once to bf16 and contracts
-it with the bf16 hidden states on MFMA with fp32 accumulation.  Two checks:
-against the exact fp64 definition (normwise max-relative < 1e-2, the size of
-bf16 rounding of G) and against the definition with G rounded to bf16 the
-same way (< 1e-4: only fp32 accumulation and rare rounding-tie differences).
+it with the bf16 hidden states on MFMA with fp32 accumulation.
+
+The parity gate is the comparison with the exact fp64 definition
+(oracle.proj_bwd on the unrounded dX_s): normwise max-relative < 1e-2, the
+size of one bf16 rounding of G.
+
+A second, tighter comparison (< 1e-4) is a MODEL OF THE KERNEL, not an
+independent pin: `_g_bf16` reproduces the kernel's own fp32 operation order
+for G and its bf16 rounding, and only the contraction is then done by the
+oracle.  It checks that nothing but the accumulation order differs once the
+rounding of G is taken as given; it says nothing about whether that rounding
+is right, which only the 1e-2 comparison does.
 """
 import numpy as np
 import pytest
@@ -55,7 +63,8 @@ def test_proj_bwd_small(gpu_lib, B, n, dm, H, d, rope):
     h64 = widen(h, "bf16")
     exact = oracle.proj_bwd(h64, dx.astype(np.float64), c, s)
     assert normwise_max_rel(got, exact) < 1e-2
-    # G rounded to bf16 like the kernel: the contraction itself agrees to fp32 accumulation
+    # Kernel model (not a pin): G rounded to bf16 in the kernel's own fp32
+    # order, so that only the contraction's accumulation order differs.
     g = _g_bf16(dx, c, s)
     same_rounding = oracle.proj_bwd(h64, g)
     assert normwise_max_rel(got, same_rounding) < 1e-4
