@@ -129,11 +129,15 @@ def kernel_kind(name: str) -> str:
     return "other"
 
 
+def _find(d: str, suffix: str):
+    import glob
+    return sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+
+
 def _csv_rows(d: str, suffix: str):
     import csv
-    import glob
     rows = []
-    for path in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+    for path in _find(d, suffix):
         with open(path, newline="") as f:
             rows.extend(csv.DictReader(f))
     if not rows:
@@ -141,14 +145,52 @@ def _csv_rows(d: str, suffix: str):
     return rows
 
 
+def _db_query(d: str, sql: str):
+    """Rows of `sql` over every rocprofv3 SQLite output (*_results.db) under d."""
+    import sqlite3
+    out = []
+    for path in _find(d, "_results.db"):
+        con = sqlite3.connect(path)
+        try:
+            out.extend(con.execute(sql).fetchall())
+        finally:
+            con.close()
+    return out
+
+
+def _trace_stats(d: str):
+    """[(kernel name, calls, avg ns, min ns, max ns, total ns)] of a --kernel-trace run (SQLite or CSV output)."""
+    if _find(d, "_results.db"):
+        rows = _db_query(d, "select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+                            "from kernels group by name")
+    else:
+        def col(r, *names):
+            for k in names:
+                for kk in r:
+                    if kk.lower().replace("_", "") == k.lower().replace("_", ""):
+                        return r[kk]
+            raise SystemExit(f"column {names} not in {list(r)}")
+        rows = [(col(r, "Name", "KernelName", "Kernel_Name"), int(col(r, "Calls")), float(col(r, "AverageNs")),
+                 float(col(r, "MinNs")), float(col(r, "MaxNs")), float(col(r, "TotalDurationNs")))
+                for r in _csv_rows(d, "kernel_stats.csv")]
+    if not rows:
+        raise SystemExit(f"no kernel trace under {d}")
+    return sorted(rows, key=lambda r: -r[5])
+
+
 def _pmc_all(dirs):
     """Per-dispatch counter values from rocprofv3 --pmc runs: {counter: {kernel: [value per dispatch]}}.
     Rows of one (dispatch, counter) are summed (covers per-dimension rows as well as aggregated ones)."""
     per = {}
     for d in dirs:
-        for r in _csv_rows(d, "counter_collection.csv"):
-            key = (r["Counter_Name"], r["Kernel_Name"], d, r.get("Dispatch_Id", r.get("Correlation_Id")))
-            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        if _find(d, "_results.db"):
+            rows = _db_query(d, "select counter_name, kernel_name, dispatch_id, value from counters_collection")
+        else:
+            rows = [(r["Counter_Name"], r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id")),
+                     r["Counter_Value"]) for r in _csv_rows(d, "counter_collection.csv")]
+        for ctr, name, disp, val in rows:
+            key = (ctr, name, d, disp)
+            per[key] = per.get(key, 0.0) + float(val)
     out = {}
     for (ctr, name, _, _), v in per.items():
         out.setdefault(ctr, {}).setdefault(name, []).append(v)
@@ -165,31 +207,24 @@ ALG_UNITS = {"lse_fwd": 2, "kl_rows": 3, "kl_cols": 1}
 def summarize(trace_dir: str, copy_mib: str, pmc_dirs, cmds: str) -> str:
     import linear_memory_relation_amd as lmr
     copy_bytes = int(copy_mib) * 2 ** 20
-    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    stats = _trace_stats(trace_dir)
     pmc = _pmc_all(pmc_dirs)
     lines = ["# Kernel time, hardware counters and HBM traffic of one relation-KL step (llama2_16k workload)", ""]
     lines += ["Workload: B=1, H=32, n=16384, d=128, bf16, maps Q/Q, K/K, V/V, causal, split dX mode.", ""]
     lines += [f"Library: {lmr.version()}", ""]
-    lines += ["Commands (run from the repository root; rocprofv3 wrote CSV under the -d directory):", "", "```"]
+    lines += ["Commands (run from the repository root; rocprofv3 wrote its output under the -d directory):", "",
+              "```"]
     lines += [c for c in cmds.split(";;") if c] + ["```", ""]
     lines += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", ""]
     lines += ["| kernel | kind | calls | avg ms | min ms | max ms | share of GPU time |", "|---|---|---|---|---|---|---|"]
-
-    def col(r, *names):
-        for k in names:
-            for kk in r:
-                if kk.lower().replace("_", "") == k.lower().replace("_", ""):
-                    return r[kk]
-        raise SystemExit(f"column {names} not in {list(r)}")
+    total = sum(r[5] for r in stats)
     avg_ns = {}
-    for r in sorted(stats, key=lambda r: -float(col(r, "TotalDurationNs"))):
-        name = col(r, "Name", "KernelName", "Kernel_Name")
+    for name, calls, avg, mn, mx, tot in stats:
         kind = kernel_kind(name)
         if kind in ALG_UNITS:
-            avg_ns[kind] = float(col(r, "AverageNs"))
-        lines.append(f"| `{name[:90]}` | {kind} | {col(r, 'Calls')} | "
-                     f"{float(col(r, 'AverageNs')) / 1e6:.4f} | {float(col(r, 'MinNs')) / 1e6:.4f} | "
-                     f"{float(col(r, 'MaxNs')) / 1e6:.4f} | {float(col(r, 'Percentage')):.2f}% |")
+            avg_ns[kind] = float(avg)
+        lines.append(f"| `{name[:90]}` | {kind} | {calls} | {avg / 1e6:.4f} | {mn / 1e6:.4f} | {mx / 1e6:.4f} | "
+                     f"{100 * tot / total:.2f}% |")
 
     def by_kind(ctr):
         """Mean per dispatch of a counter, by kernel kind (sweep kernels only)."""
@@ -207,6 +242,7 @@ def summarize(trace_dir: str, copy_mib: str, pmc_dirs, cmds: str) -> str:
     mops = by_kind("SQ_INSTS_VALU_MFMA_MOPS_BF16")
     nmfma = by_kind("SQ_INSTS_MFMA")
     valu = by_kind("SQ_ACTIVE_INST_VALU")
+    coex = by_kind("SQ_VALU_MFMA_COEXEC_CYCLES")
     if gui and busy:
         import linear_memory_relation_amd  # noqa: F401  (version printed above)
         from synth_inputs import WORKLOADS
@@ -221,10 +257,13 @@ def summarize(trace_dir: str, copy_mib: str, pmc_dirs, cmds: str) -> str:
                   "(AMD's VALUBusy expression);",
                   "- `executed flop` = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 and, as a cross-check, SQ_INSTS_MFMA x "
                   f"{FLOPS_PER_MFMA} (one v_mfma_f32_32x32x16_bf16);",
+                  "- `co-issue` = sum of SQ_VALU_MFMA_COEXEC_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs): "
+                  "cycles in which a SIMD issued a VALU instruction while its MFMA unit was busy;",
                   "- `algorithmic flop` = the kernel's share of the method's 6 GEMM-units (phase 1: 2, row sweep: 3, "
                   "column sweep: 1), one unit = 2*d*n(n+1)/2 flop per head.", ""]
-        lines += ["| kind | clock GHz | MFMA busy | VALU busy | executed flop (MOPS) | executed flop (insts) | "
-                  "algorithmic flop | executed / algorithmic |", "|---|---|---|---|---|---|---|---|"]
+        lines += ["| kind | clock GHz | MFMA busy | VALU busy | co-issue | executed flop (MOPS) | "
+                  "executed flop (insts) | algorithmic flop | executed / algorithmic |",
+                  "|---|---|---|---|---|---|---|---|---|"]
         for kind in ("lse_fwd", "kl_rows", "kl_cols"):
             if kind not in gui:
                 continue
@@ -235,10 +274,13 @@ def summarize(trace_dir: str, copy_mib: str, pmc_dirs, cmds: str) -> str:
             ef = mops.get(kind, float("nan")) * 512
             ei = nmfma.get(kind, float("nan")) * FLOPS_PER_MFMA
             af = ALG_UNITS[kind] * unit
-            lines.append(f"| {kind} | {clk:.3f} | {mb:.3f} | {vb:.3f} | {ef:.4e} | {ei:.4e} | {af:.4e} | "
+            co = coex.get(kind, float("nan")) / (g * SIMD_NUM)
+            lines.append(f"| {kind} | {clk:.3f} | {mb:.3f} | {vb:.3f} | {co:.3f} | {ef:.4e} | {ei:.4e} | {af:.4e} | "
                          f"{ef / af:.3f} |")
             machine[kind] = {"clock_ghz": clk, "mfma_busy": mb, "valu_busy": vb, "executed_flops": ef,
                              "executed_over_algorithmic": ef / af}
+            if kind in coex:
+                machine[kind]["mfma_valu_coissue"] = co
     # ---- other SQ counters, raw ---------------------------------------------
     other = [c for c in sorted(pmc) if c.startswith("SQ_") and c not in (
         "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU")]
@@ -635,12 +677,13 @@ def main():
                 "traffic": ctr.get("traffic_bytes_per_launch"),
                 "alg_flops_per_launch": fl,
                 "executed_frac": round(kern[kind]["executed_tflops"] / PEAK_BF16_TFLOPS, 4),
-                "counters": {k: ctr[k] for k in ("mfma_busy", "valu_busy", "clock_ghz", "executed_flops",
-                                                 "executed_over_algorithmic") if k in ctr} or None,
+                "counters": {k: ctr[k] for k in ("mfma_busy", "valu_busy", "mfma_valu_coissue", "clock_ghz",
+                                                 "executed_flops", "executed_over_algorithmic") if k in ctr} or None,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"}
     sweeps = [k for k in KINDS if alg[k] > 0]
     dom = max(KINDS, key=lambda k: kern[k]["share"])
     value = step_flops / (ms_step * 1e-3) / 1e12
+    roof_dom, roof_all = roof(dom), {k: roof(k) for k in sweeps}
 
     extra = {}
     del bufs
@@ -664,8 +707,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "n": w.n, "d": w.d, "heads": w.heads,
                    "maps": list(maps), "causal": True, "scale": scale, "dx_mode": "split"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": roof(dom),
-        "rooflines": {k: roof(k) for k in sweeps},
+        "roofline": roof_dom,
+        "rooflines": roof_all,
         "kernels": kern,
         "ms_per_step_one_call": round(ms_step_oneshot, 4),
         "wall_s_timed": round(wall, 3),

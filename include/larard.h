@@ -50,15 +50,26 @@
 extern "C" {
 #endif
 
+/* The _RANGE_MIN_ / _RANGE_MAX_ sentinels make every 32-bit value a valid
+ * object of the enum type, so a caller may pass any int (e.g. from another
+ * language) without undefined behaviour; the library rejects all values but
+ * the named ones. */
 typedef enum {
   LARARD_OK = 0,
   LARARD_E_INVALID = 1,     /* null pointer, bad size, bad scale, misalignment */
   LARARD_E_UNSUPPORTED = 2, /* head dim, dtype or mode not built */
   LARARD_E_WORKSPACE = 3,   /* workspace too small or misaligned */
-  LARARD_E_HIP = 4          /* a HIP runtime call or kernel launch failed */
+  LARARD_E_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  LARARD_STATUS_RANGE_MIN_ = -0x7fffffff - 1,
+  LARARD_STATUS_RANGE_MAX_ = 0x7fffffff
 } larard_status;
 
-typedef enum { LARARD_BF16 = 0, LARARD_FP32 = 1 } larard_dtype;
+typedef enum {
+  LARARD_BF16 = 0,
+  LARARD_FP32 = 1,
+  LARARD_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  LARARD_DTYPE_RANGE_MAX_ = 0x7fffffff
+} larard_dtype;
 
 /* How phase 2 produces the column term dZ^T X_s of the gradient.
  *   SPLIT : a second, column-owned sweep recomputes the logit tiles and adds

@@ -130,6 +130,56 @@ larard_status check_phase2(const void* x_t, const void* x_s, larard_dtype dtype,
   return LARARD_OK;
 }
 
+// Validation of larard_loss and its allocation-free variant (no HIP state touched).
+larard_status check_loss(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H, int64_t n,
+                         int64_t d, float scale, float loss_scale, const float* loss, const float* dx_s,
+                         int dx_mode) {
+  larard_status s = check_common(x_t, x_s, dtype, B, H, n, d, scale);
+  if (s != LARARD_OK) return s;
+  if ((s = check_dx_mode(dx_mode)) != LARARD_OK) return s;
+  if (!std::isfinite(loss_scale)) return fail(LARARD_E_INVALID, "loss_scale must be finite");
+  if (loss == nullptr || !aligned(loss, 4)) return fail(LARARD_E_INVALID, "loss must be a 4-byte aligned device pointer");
+  if (dx_s != nullptr && !aligned(dx_s, 16)) return fail(LARARD_E_INVALID, "dx_s must be 16-byte aligned");
+  return LARARD_OK;
+}
+
+larard_status zero_loss(float* loss, hipStream_t st) {
+  const hipError_t e = lmr::launch_zero_scalar(loss, st);
+  return e == hipSuccess ? LARARD_OK : hip_fail(e, "zero loss launch");
+}
+
+// Whole path of one map on a validated call, with scratch ws (256-byte aligned,
+// >= larard_workspace_bytes): phase 1, phase 2 (or the forward-only sweep) and
+// the fp64 reduction.  Every scratch byte read is written earlier in the same
+// call (LSE and row KL of every row, one partial per head), so ws needs no
+// clearing.
+larard_status run_loss(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H, int64_t n,
+                       int64_t d, float scale, int causal, float loss_scale, char* ws, float* loss, float* dx_s,
+                       hipStream_t st) {
+  size_t off[4];
+  larard_status s = larard_workspace_layout(dtype, B, H, n, off);
+  if (s != LARARD_OK) return s;
+  lmr::SweepArgs a = make_args(x_t, x_s, dtype, B, H, n, d, scale, causal);
+  a.lse_t = ws + off[0];
+  a.lse_s = ws + off[1];
+  a.row_kl = reinterpret_cast<float*>(ws + off[2]);
+  double* partials = reinterpret_cast<double*>(ws + off[3]);
+  hipError_t e;
+  if (dx_s == nullptr) {
+    // Loss only: LSE and row KL in one phase-1 sweep.
+    e = lmr::launch_kl_fwd(a, st);
+    if (e != hipSuccess) return hip_fail(e, "kl_fwd launch");
+  } else {
+    e = lmr::launch_lse_fwd(a, st);
+    if (e != hipSuccess) return hip_fail(e, "lse_fwd launch");
+    a.dx = dx_s;
+    if ((s = run_kl_bwd(a, loss_scale, st)) != LARARD_OK) return s;
+  }
+  e = lmr::launch_reduce(a.row_kl, a.bh, a.n, loss_scale, partials, loss, st);
+  if (e != hipSuccess) return hip_fail(e, "loss reduction launch");
+  return LARARD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -207,47 +257,16 @@ larard_status larard_kl_bwd(const void* x_t, const void* x_s, larard_dtype dtype
 larard_status larard_loss(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
                           int64_t n, int64_t d, float scale, int causal, float loss_scale, void* workspace,
                           size_t workspace_bytes, float* loss, float* dx_s, int dx_mode, void* stream) {
-  larard_status s = check_common(x_t, x_s, dtype, B, H, n, d, scale);
+  larard_status s = check_loss(x_t, x_s, dtype, B, H, n, d, scale, loss_scale, loss, dx_s, dx_mode);
   if (s != LARARD_OK) return s;
-  if ((s = check_dx_mode(dx_mode)) != LARARD_OK) return s;
-  if (!std::isfinite(loss_scale)) return fail(LARARD_E_INVALID, "loss_scale must be finite");
-  if (loss == nullptr || !aligned(loss, 4)) return fail(LARARD_E_INVALID, "loss must be a 4-byte aligned device pointer");
-  if (dx_s != nullptr && !aligned(dx_s, 16)) return fail(LARARD_E_INVALID, "dx_s must be 16-byte aligned");
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (n == 0) {
-    const hipError_t e = lmr::launch_zero_scalar(loss, st);
-    return e == hipSuccess ? LARARD_OK : hip_fail(e, "zero loss launch");
-  }
-  size_t off[4];
-  if ((s = larard_workspace_layout(dtype, B, H, n, off)) != LARARD_OK) return s;
+  if (n == 0) return zero_loss(loss, st);
   const size_t need = larard_workspace_bytes(dtype, B, H, n);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(LARARD_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (!aligned(workspace, 256)) return fail(LARARD_E_WORKSPACE, "workspace must be 256-byte aligned");
-  char* ws = static_cast<char*>(workspace);
-  void* lse_t = ws + off[0];
-  void* lse_s = ws + off[1];
-  float* row_kl = reinterpret_cast<float*>(ws + off[2]);
-  double* partials = reinterpret_cast<double*>(ws + off[3]);
-
-  lmr::SweepArgs a = make_args(x_t, x_s, dtype, B, H, n, d, scale, causal);
-  a.lse_t = lse_t;
-  a.lse_s = lse_s;
-  a.row_kl = row_kl;
-  hipError_t e;
-  if (dx_s == nullptr) {
-    // Loss only: LSE and row KL in one phase-1 sweep.
-    e = lmr::launch_kl_fwd(a, st);
-    if (e != hipSuccess) return hip_fail(e, "kl_fwd launch");
-  } else {
-    e = lmr::launch_lse_fwd(a, st);
-    if (e != hipSuccess) return hip_fail(e, "lse_fwd launch");
-    a.dx = dx_s;
-    if ((s = run_kl_bwd(a, loss_scale, st)) != LARARD_OK) return s;
-  }
-  e = lmr::launch_reduce(row_kl, a.bh, a.n, loss_scale, partials, loss, st);
-  if (e != hipSuccess) return hip_fail(e, "loss reduction launch");
-  return LARARD_OK;
+  return run_loss(x_t, x_s, dtype, B, H, n, d, scale, causal, loss_scale, static_cast<char*>(workspace), loss, dx_s,
+                  st);
 }
 
 larard_status larard_kl_bwd_rows(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
@@ -558,6 +577,7 @@ const char* larard_status_str(larard_status status) {
     case LARARD_E_UNSUPPORTED: return "LARARD_E_UNSUPPORTED: unsupported head dim, dtype or mode";
     case LARARD_E_WORKSPACE: return "LARARD_E_WORKSPACE: workspace too small or misaligned";
     case LARARD_E_HIP: return "LARARD_E_HIP: HIP runtime error";
+    default: break;
   }
   return "unknown larard_status";
 }

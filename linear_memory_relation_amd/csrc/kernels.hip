@@ -291,12 +291,18 @@ __device__ inline void kl_block_stat(const f32x16& St, const f32x16& Ss, float c
 }
 
 // Work item of a block in a launch over a map set.  Blocks are ordered by
-// map, then by row-block rank r (longest rows first), then by head, which is
-// the order of separate per-map launches without the gaps between them:
-// interleaving maps at every rank keeps three times as many heads in flight
-// per XCD and costs L2 hits (measured 6% slower at n = 16K).  With head
-// counts that are multiples of 8 every head's blocks stay on one XCD.  The
-// map's arguments are selected with a uniform select chain (no indexed copy).
+// map, then within a map so that the workgroups resident on one XCD at a
+// time share few heads: workgroups are handed to the 8 XCDs round-robin by
+// block index, and the workgroups of one head that run together on one XCD
+// sweep the same key tiles, which its L2 then serves once.  When the map's
+// head count is a multiple of 8, XCD x (blocks x, x+8, ...) takes its heads
+// x, x+8, ... in groups of LMR_XCD_HEADS, and runs each group's row blocks
+// rank by rank (longest rows first), heads interleaved.  Other head counts
+// use rank-major order over all heads.  The map's arguments are selected
+// with a uniform select chain (no indexed copy).
+#ifndef LMR_XCD_HEADS
+#define LMR_XCD_HEADS 0      // 0: every head of the XCD in one group (rank-major)
+#endif
 struct WorkItem {
   SweepArgs a;
   int64_t bh;   // head within the map
@@ -317,8 +323,17 @@ __device__ inline WorkItem decode(const MapSet& S, int nblk) {
     }
   }
   const int64_t local = bid - (int64_t)nblk * h0, heads = h1 - h0;
-  w.r = (int)(local / heads);
-  w.bh = local % heads;
+  const int64_t q = heads / 8;                        // heads per XCD
+  const int64_t g = LMR_XCD_HEADS > 0 && LMR_XCD_HEADS < q && q % LMR_XCD_HEADS == 0 ? LMR_XCD_HEADS : q;
+  if (heads % 8 == 0) {
+    const int64_t x = local % 8, slot = local / 8;    // XCD and position in its queue
+    const int64_t grp = slot / (g * nblk), rem = slot % (g * nblk);
+    w.r = (int)(rem / g);
+    w.bh = x + 8 * (grp * g + rem % g);
+  } else {
+    w.r = (int)(local / heads);
+    w.bh = local % heads;
+  }
   return w;
 }
 
