@@ -38,7 +38,9 @@
  *     launch, and on a validation error nothing is launched or written.
  *     A failing HIP call returns LARARD_E_HIP; its text is available from
  *     larard_last_error() on the calling thread.
- *   - The library holds no mutable global state and is thread-safe.
+ *   - The library is thread-safe.  Its only mutable global state belongs to
+ *     larard_loss_noalloc: a static device scratch array per GPU and a
+ *     mutex-guarded cache of its address per device.
  */
 #ifndef LARARD_H
 #define LARARD_H
@@ -170,6 +172,29 @@ larard_status larard_loss(const void* x_t, const void* x_s, larard_dtype dtype,
                           float scale, int causal, float loss_scale,
                           void* workspace, size_t workspace_bytes,
                           float* loss, float* dx_s, int dx_mode, void* stream);
+
+/* Allocation-free larard_loss, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and kernels as larard_loss
+ * without the workspace pair: LSE_t, LSE_s, row_kl and the partial sums live
+ * in a static device array of LARARD_NOALLOC_SCRATCH_BYTES bytes that the
+ * library's device code carries (one copy per GPU, held until the process
+ * ends).  Its device address is looked up once per device, with that device
+ * current, on the first call there; nothing is allocated, by this call or by
+ * any routine it calls.
+ *   - Shapes whose larard_workspace_bytes(dtype, B, H, n) exceeds
+ *     LARARD_NOALLOC_SCRATCH_BYTES are rejected with LARARD_E_WORKSPACE
+ *     (64 MiB: B*H*n up to ~3.3 million rows, e.g. 32 heads at n = 64K).
+ *   - Every call on one GPU shares that GPU's array and leaves its own
+ *     statistics there.  Calls that overlap in time on one GPU (other
+ *     streams, other threads) race on it and must be ordered by the caller.
+ *   - No clearing is needed between calls: every scratch byte a call reads is
+ *     written earlier by the same call. */
+#define LARARD_NOALLOC_SCRATCH_BYTES (64u << 20)
+larard_status larard_loss_noalloc(const void* x_t, const void* x_s, larard_dtype dtype,
+                                  int64_t B, int64_t H, int64_t n, int64_t d,
+                                  float scale, int causal, float loss_scale,
+                                  float* loss, float* dx_s, int dx_mode, void* stream);
 
 /* ---------------------------------------------------------------------------
  * General relation X != Y (notes page, "Key designs" item 1 defines the map

@@ -7,4 +7,5 @@ from .binding import (  # noqa: F401
     kl_bwd_cols, kl_bwd_rows, reduce_loss,
     load, loss, lse_fwd, source_id, stat_dtype, version, workspace_bytes, workspace_layout,
     xy_kl_bwd, xy_kl_fwd, xy_loss, xy_lse_fwd, LarardMap, multi_loss, multi_workspace_bytes, proj_bwd,
+    loss_noalloc, NOALLOC_SCRATCH_BYTES,
 )

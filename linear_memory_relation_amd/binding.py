@@ -59,6 +59,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.larard_loss.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, f32, vp, ctypes.c_size_t,
                                 vp, vp, i32, vp]
     lib.larard_loss.restype = i32
+    lib.larard_loss_noalloc.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, f32, vp, vp, i32, vp]
+    lib.larard_loss_noalloc.restype = i32
     lib.larard_xy_lse_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, vp]
     lib.larard_xy_lse_fwd.restype = i32
     lib.larard_xy_kl_fwd.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, vp, vp]
@@ -317,6 +319,32 @@ def loss(xt: torch.Tensor, xs: torch.Tensor, scale: Optional[float] = None, caus
                             float(loss_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
                             _ptr(out), _ptr(dx), int(dx_mode), _stream())
     _check(st, "larard_loss")
+    return out, dx
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20      # LARARD_NOALLOC_SCRATCH_BYTES of larard.h
+
+
+def loss_noalloc(xt: torch.Tensor, xs: torch.Tensor, scale: Optional[float] = None, causal: bool = True,
+                 loss_scale: float = 1.0, need_dx: bool = True, dx_mode: int = DX_AUTO,
+                 out: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None
+                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """larard_loss_noalloc: the whole path for one map with the library's static device scratch
+    (no workspace; the caller's out/dx are the only buffers).  Same results as `loss`."""
+    B, H, n, d = _shape(xt, xs)
+    scale = default_scale(d) if scale is None else float(scale)
+    if not need_dx:
+        dx = None
+    _need(out, "out", (), torch.float32, optional=True)
+    _need(dx, "dx", (B, H, n, d), torch.float32, optional=True)
+    _on_gpu(xt, xs, out, dx)
+    if out is None:
+        out = torch.empty((), dtype=torch.float32, device=xt.device)
+    if need_dx and dx is None:
+        dx = torch.empty((B, H, n, d), dtype=torch.float32, device=xt.device)
+    st = load().larard_loss_noalloc(_ptr(xt), _ptr(xs), _dtype_code(xt), B, H, n, d, scale, int(causal),
+                                    float(loss_scale), _ptr(out), _ptr(dx), int(dx_mode), _stream())
+    _check(st, "larard_loss_noalloc")
     return out, dx
 
 

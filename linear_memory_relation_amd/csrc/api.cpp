@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "larard.h"
@@ -180,6 +181,35 @@ larard_status run_loss(const void* x_t, const void* x_s, larard_dtype dtype, int
   return LARARD_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of larard_loss_noalloc: one array per GPU, loaded with the library's
+// device code and held until the process ends.  In host code `scratch` only
+// names the symbol; its device address (one per GPU) comes from
+// hipGetSymbolAddress, looked up once per device and cached.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[LARARD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+larard_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LARARD_E_INVALID, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || !aligned(p, 256)) return fail(LARARD_E_HIP, "scratch symbol has no 256-byte aligned address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LARARD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -267,6 +297,23 @@ larard_status larard_loss(const void* x_t, const void* x_s, larard_dtype dtype, 
   if (!aligned(workspace, 256)) return fail(LARARD_E_WORKSPACE, "workspace must be 256-byte aligned");
   return run_loss(x_t, x_s, dtype, B, H, n, d, scale, causal, loss_scale, static_cast<char*>(workspace), loss, dx_s,
                   st);
+}
+
+larard_status larard_loss_noalloc(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
+                                  int64_t n, int64_t d, float scale, int causal, float loss_scale, float* loss,
+                                  float* dx_s, int dx_mode, void* stream) {
+  larard_status s = check_loss(x_t, x_s, dtype, B, H, n, d, scale, loss_scale, loss, dx_s, dx_mode);
+  if (s != LARARD_OK) return s;
+  const size_t need = larard_workspace_bytes(dtype, B, H, n);
+  if (need > (size_t)LARARD_NOALLOC_SCRATCH_BYTES)
+    return fail(LARARD_E_WORKSPACE, "larard_loss_noalloc: B*H*n = %lld rows need %zu bytes of scratch, above the "
+                "library's static %zu bytes; use larard_loss with a caller workspace",
+                (long long)(B * H * n), need, (size_t)LARARD_NOALLOC_SCRATCH_BYTES);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n == 0) return zero_loss(loss, st);
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != LARARD_OK) return s;
+  return run_loss(x_t, x_s, dtype, B, H, n, d, scale, causal, loss_scale, static_cast<char*>(ws), loss, dx_s, st);
 }
 
 larard_status larard_kl_bwd_rows(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,

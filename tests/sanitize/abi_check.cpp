@@ -85,6 +85,10 @@ int main() {
                                       ffake(), 0, nullptr), LARARD_E_WORKSPACE);
   expect("loss atomic", larard_loss(fake(), fake(), bf, 1, 2, 64, 128, 0.1f, 1, 1.f, fake(), need, ffake(), ffake(),
                                     LARARD_DX_ATOMIC, nullptr), LARARD_E_UNSUPPORTED);
+  expect("noalloc limit", larard_loss_noalloc(fake(), fake(), bf, 1, 64, 65536, 64, 0.1f, 1, 1.f, ffake(), ffake(), 0,
+                                              nullptr), LARARD_E_WORKSPACE);
+  expect("noalloc loss null", larard_loss_noalloc(fake(), fake(), bf, 1, 2, 64, 64, 0.1f, 1, 1.f, nullptr, ffake(), 0,
+                                                  nullptr), LARARD_E_INVALID);
 
   // cross relation
   expect("xy null y", larard_xy_lse_fwd(fake(), fake(), nullptr, fake(), bf, 1, 2, 64, 128, 0.1f, 1, fake(), fake(),

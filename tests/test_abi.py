@@ -256,3 +256,24 @@ def test_dx_mode_status(lib, mode, code):
     assert _loss(lib, mode=mode) == code
     if code == 2:
         assert "ATOMIC" in lib.larard_last_error().decode()
+
+
+def test_noalloc_validation_before_any_device_access(lib):
+    """larard_loss_noalloc checks its arguments and the static scratch limit before it looks up
+    the scratch address or launches anything."""
+    import linear_memory_relation_amd as lmr
+
+    def call(**kw):
+        a = dict(xt=FAKE, xs=FAKE, dt=0, B=1, H=2, n=64, d=128, scale=0.1, causal=1, lscale=1.0,
+                 loss=FAKE, dx=FAKE, mode=0)
+        a.update(kw)
+        return lib.larard_loss_noalloc(a["xt"], a["xs"], a["dt"], a["B"], a["H"], a["n"], a["d"], a["scale"],
+                                       a["causal"], a["lscale"], a["loss"], a["dx"], a["mode"], None)
+    assert lmr.workspace_bytes(1, 64, 65536) > lmr.NOALLOC_SCRATCH_BYTES >= lmr.workspace_bytes(1, 32, 65536)
+    assert call(H=64, n=65536) == 3
+    assert "scratch" in lib.larard_last_error().decode()
+    assert call(loss=None) == 1
+    assert call(dx=FAKE + 4) == 1
+    assert call(mode=2) == 2
+    assert call(d=96) == 2
+    assert call(xt=None) == 1
