@@ -120,6 +120,8 @@ def library_source_id() -> str:
 def kernel_kind(name: str) -> str:
     if "lse_fwd_kernel" in name:
         return "lse_fwd"
+    if "kl_fused_kernel" in name:
+        return "kl_bwd"
     if "kl_sweep_kernel" in name:
         return "kl_rows" if ", 0, " in name else "kl_cols"
     if "reduce_rows_kernel" in name or "reduce_final_kernel" in name:
@@ -201,7 +203,7 @@ def _pmc_all(dirs):
 # 256 CUs, 4 SIMDs each, 8 XCDs (GRBM_GUI_ACTIVE is counted once per XCD).
 CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
 FLOPS_PER_MFMA = 2 * 32 * 32 * 16        # v_mfma_f32_32x32x16_bf16
-ALG_UNITS = {"lse_fwd": 2, "kl_rows": 3, "kl_cols": 1}
+ALG_UNITS = {"lse_fwd": 2, "kl_bwd": 4, "kl_rows": 2, "kl_cols": 2}
 
 
 def summarize(trace_dir: str, copy_mib: str, pmc_dirs, cmds: str) -> str:
@@ -210,7 +212,7 @@ def summarize(trace_dir: str, copy_mib: str, pmc_dirs, cmds: str) -> str:
     stats = _trace_stats(trace_dir)
     pmc = _pmc_all(pmc_dirs)
     lines = ["# Kernel time, hardware counters and HBM traffic of one relation-KL step (llama2_16k workload)", ""]
-    lines += ["Workload: B=1, H=32, n=16384, d=128, bf16, maps Q/Q, K/K, V/V, causal, split dX mode.", ""]
+    lines += ["Workload: B=1, H=32, n=16384, d=128, bf16, maps Q/Q, K/K, V/V, causal.", ""]
     lines += [f"Library: {lmr.version()}", ""]
     lines += ["Commands (run from the repository root; rocprofv3 wrote its output under the -d directory):", "",
               "```"]
@@ -259,12 +261,12 @@ def summarize(trace_dir: str, copy_mib: str, pmc_dirs, cmds: str) -> str:
                   f"{FLOPS_PER_MFMA} (one v_mfma_f32_32x32x16_bf16);",
                   "- `co-issue` = sum of SQ_VALU_MFMA_COEXEC_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs): "
                   "cycles in which a SIMD issued a VALU instruction while its MFMA unit was busy;",
-                  "- `algorithmic flop` = the kernel's share of the method's 6 GEMM-units (phase 1: 2, row sweep: 3, "
-                  "column sweep: 1), one unit = 2*d*n(n+1)/2 flop per head.", ""]
+                  "- `algorithmic flop` = the kernel's share of the method's 6 GEMM-units (phase 1: 2; phase 2: 4, "
+                  "credited 2 to each split sweep, which executes 3), one unit = 2*d*n(n+1)/2 flop per head.", ""]
         lines += ["| kind | clock GHz | MFMA busy | VALU busy | co-issue | executed flop (MOPS) | "
                   "executed flop (insts) | algorithmic flop | executed / algorithmic |",
                   "|---|---|---|---|---|---|---|---|---|"]
-        for kind in ("lse_fwd", "kl_rows", "kl_cols"):
+        for kind in ALG_UNITS:
             if kind not in gui:
                 continue
             g = gui[kind] / XCD_NUM
@@ -481,38 +483,51 @@ def make_buffers(w, dev):
     return maps, bufs
 
 
-KINDS = ["lse_fwd", "kl_rows", "kl_cols", "reduce"]
+# Kernels of one map's step in each phase-2 mode (the events bracket each).
+KINDS = {"fused": ["lse_fwd", "kl_bwd", "reduce"], "split": ["lse_fwd", "kl_rows", "kl_cols", "reduce"]}
+# GEMM-units per head-map: algorithmic (the method's 6: phase 1 does 2, phase 2 does 4) and executed
+# (phase 2 computes its logit tiles twice, once for the row term and once for the column term).  In
+# split mode each of phase 2's two sweeps executes 3 (both logit tiles and one contraction) and is
+# credited with half of phase 2's 4.
+ALG = {"lse_fwd": 2, "kl_bwd": 4, "kl_rows": 2, "kl_cols": 2, "reduce": 0}
+EXE = {"lse_fwd": 2, "kl_bwd": 6, "kl_rows": 3, "kl_cols": 3, "reduce": 0}
 
 
-def run_steps(bufs, scale, steps, warmup, events=True):
-    """Warm up, then time `steps` steps (each map: phase 1, row sweep, column sweep, reduction,
-    as larard_loss launches them) with HIP events on the launch stream.  Returns
-    (ms per step, per-kernel times in ms, wall seconds of the timed region)."""
+def run_steps(bufs, scale, steps, warmup, events=True, mode="split"):
+    """Warm up, then time `steps` steps (each map: phase 1, phase 2 -- one fused sweep, or the
+    row and column sweeps in split mode -- and the loss reduction, as larard_loss launches them)
+    with HIP events on the launch stream.  Returns (ms per step, per-kernel times in ms,
+    total ms, wall seconds of the timed region)."""
     import torch
     import linear_memory_relation_amd as lmr
+    kinds = KINDS[mode]
 
     def step(ev=None):
         for b in bufs:
             a = (b["xt"], b["xs"])
-            if ev is not None:
-                ev[b["name"]][0].record()
+            marks = iter(ev[b["name"]]) if ev is not None else None
+
+            def mark():
+                if marks is not None:
+                    next(marks).record()
+            mark()
             lmr.lse_fwd(*a, scale, True, b["lse_t"], b["lse_s"])
-            if ev is not None:
-                ev[b["name"]][1].record()
-            lmr.kl_bwd_rows(*a, b["lse_t"], b["lse_s"], b["row_kl"], b["dx"], scale, True, 1.0)
-            if ev is not None:
-                ev[b["name"]][2].record()
-            lmr.kl_bwd_cols(*a, b["lse_t"], b["lse_s"], b["dx"], scale, True, 1.0)
-            if ev is not None:
-                ev[b["name"]][3].record()
+            mark()
+            if mode == "fused":
+                lmr.kl_bwd(*a, b["lse_t"], b["lse_s"], scale, True, 1.0, dx_mode=lmr.DX_FUSED,
+                           row_kl=b["row_kl"], dx=b["dx"])
+            else:
+                lmr.kl_bwd_rows(*a, b["lse_t"], b["lse_s"], b["row_kl"], b["dx"], scale, True, 1.0)
+                mark()
+                lmr.kl_bwd_cols(*a, b["lse_t"], b["lse_s"], b["dx"], scale, True, 1.0)
+            mark()
             lmr.reduce_loss(b["row_kl"], b["partials"], b["loss"], 1.0)
-            if ev is not None:
-                ev[b["name"]][4].record()
+            mark()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [{b["name"]: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for b in bufs}
+    ev = [{b["name"]: [torch.cuda.Event(enable_timing=True) for _ in range(len(kinds) + 1)] for b in bufs}
           for _ in range(steps)] if events else [None] * steps
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -524,12 +539,12 @@ def run_steps(bufs, scale, steps, warmup, events=True):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
-    per_kernel = {k: [] for k in KINDS}
+    per_kernel = {k: [] for k in kinds}
     if events:
         for k in range(steps):
             for b in bufs:
                 e = ev[k][b["name"]]
-                for j, kind in enumerate(KINDS):
+                for j, kind in enumerate(kinds):
                     per_kernel[kind].append(e[j].elapsed_time(e[j + 1]))
     return total_ms / steps, per_kernel, total_ms, wall
 
@@ -552,6 +567,25 @@ def memory_report(bufs, base_alloc, peak_alloc, free_before, free_after_alloc, f
             "dense_fp32_map_bytes_one_matrix": int(sum(4 * b["B"] * b["H"] * b["n"] ** 2 for b in bufs))}
 
 
+def time_fused_maps(bufs, scale, steps, warmup):
+    """ms per step of the same step with every map in one launch per phase (larard_multi_loss)."""
+    import torch
+    import linear_memory_relation_amd as lmr
+    mlist = [(b["xt"], b["xs"], 1.0, b["dx"]) for b in bufs]
+    wsm = torch.empty(lmr.multi_workspace_bytes(mlist), dtype=torch.uint8, device=bufs[0]["xt"].device)
+    out = torch.empty((), dtype=torch.float32, device=bufs[0]["xt"].device)
+    for _ in range(warmup):
+        lmr.multi_loss(mlist, scale, True, 1.0, workspace=wsm, out=out)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        lmr.multi_loss(mlist, scale, True, 1.0, workspace=wsm, out=out)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
 def extra_workload(name, args, dev):
     """ms/step, TFLOP/s and memory of one more workload, timed like the headline one."""
     import gc
@@ -569,13 +603,16 @@ def extra_workload(name, args, dev):
     ms, per_kernel, _, _ = run_steps(bufs, w.scale, args.extra_steps, 1)
     free_after_steps = torch.cuda.mem_get_info()[0]
     peak = torch.cuda.max_memory_allocated() - base_alloc
+    memory = memory_report(bufs, base_alloc, peak, free_before, free_after_alloc, free_after_steps)
     flops = sum(6 * units(b) for b in bufs)
+    ms_maps = time_fused_maps(bufs, w.scale, args.extra_steps, 1)
     out = {"workload": name, "B": w.B, "n": w.n, "d": w.d, "heads": w.heads, "steps": args.extra_steps,
            "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
            "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
            "kernels_avg_ms": {k: round(float(np.mean(v)), 4) for k, v in per_kernel.items()},
+           "fused_maps_ms_per_step": round(ms_maps, 4),
            "losses": {b["name"]: float(b["loss"].cpu()) for b in bufs},
-           "memory": memory_report(bufs, base_alloc, peak, free_before, free_after_alloc, free_after_steps)}
+           "memory": memory}
     del bufs
     gc.collect()
     torch.cuda.empty_cache()
@@ -623,8 +660,15 @@ def main():
 
     # Timed region: K steps with HIP events around every kernel, on the stream
     # the kernels are launched on (torch's current stream).
-    ms_step, per_kernel, total_ms, wall = run_steps(bufs, scale, args.steps, args.warmup)
+    ms_step, per_kernel, total_ms, wall = run_steps(bufs, scale, args.steps, args.warmup, mode="split")
     free_after_steps = torch.cuda.mem_get_info()[0]
+    # The same step with phase 2 as the fused single sweep, timed alike (the
+    # other mode larard_kl_bwd offers; AUTO takes the split one).
+    ms_fused, per_fused, _, _ = run_steps(bufs, scale, args.steps, 1, mode="fused")
+    phase2_fused = {"ms_per_step": round(ms_fused, 4),
+                    "kernels_avg_ms": {k: round(float(np.mean(v)), 4) for k, v in per_fused.items()},
+                    "what": "phase 2 as one launch per map (LARARD_DX_FUSED): each row block's row and column "
+                            "terms in one sweep, dX_s stored once"}
     peak_alloc = torch.cuda.max_memory_allocated() - base_alloc
     memory = memory_report(bufs, base_alloc, peak_alloc, free_before, free_after_alloc, free_after_steps)
 
@@ -649,17 +693,14 @@ def main():
         fwd_info, proj, cross, fused_info = extra_sections(args, bufs, w, scale, dev, units, step_flops)
 
     # Algorithmic work.  Per head-map P = n(n+1)/2 unmasked pairs, one
-    # contraction = 2*d*P flops.  Phase 1: 2 contractions; the row sweep
-    # carries phase 2's recompute (2) and the row term (1); the column sweep's
-    # algorithmic share is the column term (1) -- its recompute is split-mode
-    # overhead and is not counted.
-    alg = {"lse_fwd": 2, "kl_rows": 3, "kl_cols": 1, "reduce": 0}
-    exe = {"lse_fwd": 2, "kl_rows": 3, "kl_cols": 3, "reduce": 0}
+    # contraction (GEMM-unit) = 2*d*P flops.  Phase 1: 2 units; phase 2: 4
+    # (the logit recompute of both maps, the row term and the column term),
+    # executed as 6 because phase 2 forms every logit tile twice.
     kern = {}
-    for kind in KINDS:
+    for kind in KINDS["split"]:
         t = float(np.mean(per_kernel[kind]))
-        fl = np.mean([alg[kind] * units(b) for b in bufs])
-        fe = np.mean([exe[kind] * units(b) for b in bufs])
+        fl = np.mean([ALG[kind] * units(b) for b in bufs])
+        fe = np.mean([EXE[kind] * units(b) for b in bufs])
         kern[kind] = {"avg_ms": t, "share": float(np.sum(per_kernel[kind]) / total_ms),
                       "alg_tflops": fl / (t * 1e-3) / 1e12 if fl else 0.0,
                       "executed_tflops": fe / (t * 1e-3) / 1e12 if fe else 0.0}
@@ -669,7 +710,7 @@ def main():
     # VALU busy fractions, executed flops) come from the committed rocprofv3
     # summary when it was taken on a library built from the same sources.
     def roof(kind):
-        fl = float(np.mean([alg[kind] * units(b) for b in bufs]))
+        fl = float(np.mean([ALG[kind] * units(b) for b in bufs]))
         ach = fl / (kern[kind]["avg_ms"] * 1e-3) / 1e12
         ctr = recorded_counters(kind, w.name)
         return {"kernel": kind, "bound": "mfma", "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS,
@@ -680,8 +721,8 @@ def main():
                 "counters": {k: ctr[k] for k in ("mfma_busy", "valu_busy", "mfma_valu_coissue", "clock_ghz",
                                                  "executed_flops", "executed_over_algorithmic") if k in ctr} or None,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"}
-    sweeps = [k for k in KINDS if alg[k] > 0]
-    dom = max(KINDS, key=lambda k: kern[k]["share"])
+    sweeps = [k for k in KINDS["split"] if ALG[k] > 0]
+    dom = max(KINDS["split"], key=lambda k: kern[k]["share"])
     value = step_flops / (ms_step * 1e-3) / 1e12
     roof_dom, roof_all = roof(dom), {k: roof(k) for k in sweeps}
 
@@ -711,6 +752,7 @@ def main():
         "rooflines": roof_all,
         "kernels": kern,
         "ms_per_step_one_call": round(ms_step_oneshot, 4),
+        "fused_phase2": phase2_fused,
         "wall_s_timed": round(wall, 3),
         "memory": memory,
         "losses": losses,

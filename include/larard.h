@@ -74,16 +74,28 @@ typedef enum {
 } larard_dtype;
 
 /* How phase 2 produces the column term dZ^T X_s of the gradient.
- *   SPLIT : a second, column-owned sweep recomputes the logit tiles and adds
- *           the column term; deterministic, no atomics.  The only mode built.
+ *   FUSED : one launch in which each workgroup owns a block of rows k and
+ *           sweeps both the key tiles j <= k (row term) and the row tiles
+ *           i >= k (column term, the rows' role as keys), adding both into one
+ *           register accumulator and storing dX_s once; deterministic, no
+ *           atomics, every workgroup does the same work.  bf16 self-relations
+ *           only; the fp32 precision kernels and the X != Y relation run SPLIT.
+ *   SPLIT : a row-owned sweep stores the row term, then a column-owned sweep
+ *           recomputes the logit tiles and adds the column term;
+ *           deterministic, no atomics.
  *   ATOMIC: not built; every call that passes it returns
  *           LARARD_E_UNSUPPORTED.  (A row sweep that adds its column partials
  *           with fp32 atomics must add B*H*n^2 bytes per map with 256-row
  *           workgroups -- 8.6 GB at n = 16K, H = 32 -- and coalesced fp32
  *           atomic adds sustain ~1.4 TB/s on MI355X, longer than the
  *           split's whole second sweep.)
- *   AUTO  : SPLIT. */
-typedef enum { LARARD_DX_AUTO = 0, LARARD_DX_SPLIT = 1, LARARD_DX_ATOMIC = 2 } larard_dx_mode;
+ *   AUTO  : SPLIT, measured faster than FUSED on MI355X (16K: 6.29 against
+ *           6.60 ms per 32-head map), although FUSED moves a third less HBM
+ *           traffic.
+ * FUSED and SPLIT execute the same contractions (phase 2 computes every
+ * logit tile twice) and give the same results to fp32 rounding; each is
+ * bitwise reproducible. */
+typedef enum { LARARD_DX_AUTO = 0, LARARD_DX_SPLIT = 1, LARARD_DX_ATOMIC = 2, LARARD_DX_FUSED = 3 } larard_dx_mode;
 
 /* Bytes of workspace larard_loss needs: LSE_t and LSE_s (B*H*n fp64 each),
  * row_kl (B*H*n fp32) and B*H fp64 partial sums, each region 256-byte

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "liblarard.so")
 
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, 1, 2, 3, 4
 BF16, FP32 = 0, 1
-DX_AUTO, DX_SPLIT, DX_ATOMIC = 0, 1, 2
+DX_AUTO, DX_SPLIT, DX_ATOMIC, DX_FUSED = 0, 1, 2, 3
 
 _lib: Optional[ctypes.CDLL] = None
 

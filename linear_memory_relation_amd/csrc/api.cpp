@@ -94,15 +94,27 @@ larard_status set_cross(lmr::SweepArgs* a, const void* y_t, const void* y_s, int
 }
 
 larard_status check_dx_mode(int dx_mode) {
-  if (dx_mode == LARARD_DX_AUTO || dx_mode == LARARD_DX_SPLIT) return LARARD_OK;
+  if (dx_mode == LARARD_DX_AUTO || dx_mode == LARARD_DX_SPLIT || dx_mode == LARARD_DX_FUSED) return LARARD_OK;
   if (dx_mode == LARARD_DX_ATOMIC) return fail(LARARD_E_UNSUPPORTED, "dx_mode ATOMIC is not built");
   return fail(LARARD_E_INVALID, "unknown dx_mode %d", dx_mode);
 }
 
+// Whether phase 2 runs as the fused single sweep: bf16 self-relations with a
+// gradient, in FUSED mode.  AUTO takes the split sweeps, measured faster on
+// MI355X at 4K, 8K (GQA) and 16K; the fp32 precision kernels and the cross
+// relation always run split.
+bool use_fused(const lmr::SweepArgs& a, int dx_mode) {
+  return dx_mode == LARARD_DX_FUSED && !a.fp32 && !a.cross && a.dx != nullptr;
+}
+
 // Phase-2 launches (inputs already validated).
-larard_status run_kl_bwd(lmr::SweepArgs a, float loss_scale, hipStream_t st) {
+larard_status run_kl_bwd(lmr::SweepArgs a, float loss_scale, int dx_mode, hipStream_t st) {
   a.grad_scale = loss_scale * a.scale / (float)a.n;
   a.grad_scale_d = (double)loss_scale * (double)a.scale / (double)a.n;
+  if (use_fused(a, dx_mode)) {
+    const hipError_t e = lmr::launch_kl_fused(a, st);
+    return e == hipSuccess ? LARARD_OK : hip_fail(e, "kl_bwd fused sweep launch");
+  }
   hipError_t e = lmr::launch_kl_row(a, st);
   if (e != hipSuccess) return hip_fail(e, "kl_bwd row sweep launch");
   if ((a.cross ? a.dy : a.dx) != nullptr) {
@@ -156,7 +168,7 @@ larard_status zero_loss(float* loss, hipStream_t st) {
 // clearing.
 larard_status run_loss(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H, int64_t n,
                        int64_t d, float scale, int causal, float loss_scale, char* ws, float* loss, float* dx_s,
-                       hipStream_t st) {
+                       int dx_mode, hipStream_t st) {
   size_t off[4];
   larard_status s = larard_workspace_layout(dtype, B, H, n, off);
   if (s != LARARD_OK) return s;
@@ -174,7 +186,7 @@ larard_status run_loss(const void* x_t, const void* x_s, larard_dtype dtype, int
     e = lmr::launch_lse_fwd(a, st);
     if (e != hipSuccess) return hip_fail(e, "lse_fwd launch");
     a.dx = dx_s;
-    if ((s = run_kl_bwd(a, loss_scale, st)) != LARARD_OK) return s;
+    if ((s = run_kl_bwd(a, loss_scale, dx_mode, st)) != LARARD_OK) return s;
   }
   e = lmr::launch_reduce(a.row_kl, a.bh, a.n, loss_scale, partials, loss, st);
   if (e != hipSuccess) return hip_fail(e, "loss reduction launch");
@@ -281,7 +293,7 @@ larard_status larard_kl_bwd(const void* x_t, const void* x_s, larard_dtype dtype
   if (dx_s != nullptr && !aligned(dx_s, 16)) return fail(LARARD_E_INVALID, "dx_s must be 16-byte aligned");
   a.row_kl = row_kl;
   a.dx = dx_s;
-  return run_kl_bwd(a, loss_scale, static_cast<hipStream_t>(stream));
+  return run_kl_bwd(a, loss_scale, dx_mode, static_cast<hipStream_t>(stream));
 }
 
 larard_status larard_loss(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
@@ -296,7 +308,7 @@ larard_status larard_loss(const void* x_t, const void* x_s, larard_dtype dtype, 
     return fail(LARARD_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (!aligned(workspace, 256)) return fail(LARARD_E_WORKSPACE, "workspace must be 256-byte aligned");
   return run_loss(x_t, x_s, dtype, B, H, n, d, scale, causal, loss_scale, static_cast<char*>(workspace), loss, dx_s,
-                  st);
+                  dx_mode, st);
 }
 
 larard_status larard_loss_noalloc(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
@@ -313,7 +325,8 @@ larard_status larard_loss_noalloc(const void* x_t, const void* x_s, larard_dtype
   if (n == 0) return zero_loss(loss, st);
   void* ws = nullptr;
   if ((s = scratch_address(&ws)) != LARARD_OK) return s;
-  return run_loss(x_t, x_s, dtype, B, H, n, d, scale, causal, loss_scale, static_cast<char*>(ws), loss, dx_s, st);
+  return run_loss(x_t, x_s, dtype, B, H, n, d, scale, causal, loss_scale, static_cast<char*>(ws), loss, dx_s, dx_mode,
+                  st);
 }
 
 larard_status larard_kl_bwd_rows(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H,
@@ -410,7 +423,7 @@ larard_status larard_xy_kl_bwd(const void* x_t, const void* x_s, const void* y_t
   a.row_kl = row_kl;
   a.dx = dx_s;
   a.dy = dy_s;
-  return run_kl_bwd(a, loss_scale, static_cast<hipStream_t>(stream));
+  return run_kl_bwd(a, loss_scale, LARARD_DX_SPLIT, static_cast<hipStream_t>(stream));
 }
 
 larard_status larard_xy_loss(const void* x_t, const void* x_s, const void* y_t, const void* y_s,
@@ -450,7 +463,7 @@ larard_status larard_xy_loss(const void* x_t, const void* x_s, const void* y_t, 
     if (e != hipSuccess) return hip_fail(e, "xy_lse_fwd launch");
     a.dx = dx_s;
     a.dy = dy_s;
-    if ((s = run_kl_bwd(a, loss_scale, st)) != LARARD_OK) return s;
+    if ((s = run_kl_bwd(a, loss_scale, LARARD_DX_SPLIT, st)) != LARARD_OK) return s;
   }
   e = lmr::launch_reduce(a.row_kl, a.bh, a.n, loss_scale, partials, loss, st);
   if (e != hipSuccess) return hip_fail(e, "loss reduction launch");

@@ -799,6 +799,181 @@ __global__ __launch_bounds__(64 * NW, LMR_SWEEP_OCC) void kl_sweep_kernel(MapSet
 }
 
 // ---------------------------------------------------------------------------
+// Fused phase 2 of a self-relation: one workgroup owns a block of rows k and
+// produces their whole gradient.  It first sweeps the key tiles j <= k (the
+// row term sum_j dZ(k,j) x_j, as the row sweep above, with the row KL), then
+// the row tiles i >= k (the column term sum_i dZ(i,k) x_i, as the column
+// sweep above), adding both into one register accumulator and storing dX_s
+// once.  Every workgroup sweeps the same number of tiles (the causal
+// triangle of its row term plus the complementary triangle of its column
+// term), so the launch has no causal tail; the work executed is the split
+// mode's (the logit tiles are computed twice), without its second launch and
+// its read-modify-write of dX_s.
+// ---------------------------------------------------------------------------
+template <int D, int NW, int SW>
+__global__ __launch_bounds__(64 * NW, LMR_SWEEP_OCC) void kl_fused_kernel(MapSet maps, int nblk) {
+  constexpr int KS = D / 16, DB = D / 32, RB = 2 * D, TB = Tile<D, SW>::BYTES, kOwn = 32 * NW;
+  static_assert(SW % 32 == 0 && SW <= 64 * NW, "one thread per swept row fetches the statistics");
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][TB];
+  __shared__ float2 lstat[2][SW];          // column steps: (hi_t, hi_s) of the swept rows
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
+  const WorkItem wi = decode(maps, nblk);
+  const SweepArgs& a = wi.a;
+  const int64_t bh = wi.bh;
+  const int ob = wi.r;
+  const int n = a.n;
+  const int64_t hoff = bh * (int64_t)n * RB;
+  const char* xt = static_cast<const char*>(a.xt) + hoff;
+  const char* xs = static_cast<const char*>(a.xs) + hoff;
+  const double* glt = static_cast<const double*>(a.lse_t) + bh * n;
+  const double* gls = static_cast<const double*>(a.lse_s) + bh * n;
+  const int own0 = ob * kOwn, wown0 = own0 + 32 * wave, o = wown0 + (lane & 31);
+  const float c = a.scale * kLog2e;
+
+  bf16x8 Bt[KS], Bs[KS];
+  {
+    const char* rt = o < n ? xt + (int64_t)o * RB : nullptr;
+    const char* rs = o < n ? xs + (int64_t)o * RB : nullptr;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) { Bt[ks] = load_own(rt, ks, h); Bs[ks] = load_own(rs, ks, h); }
+  }
+  float l2t = 0.f, l2s = 0.f, lot = 0.f, los = 0.f;
+  if (o < n) {
+    split_stat(glt[o], l2t, lot);
+    split_stat(gls[o], l2s, los);
+  }
+  // Steps 0 .. r_end-1 are row tiles 0 .. r_end-1; the following steps are
+  // column tiles c_begin .. c_end-1.
+  const int r_end = (a.causal ? min(own0 + kOwn, n) - 1 : n - 1) / SW + 1;
+  const int c_begin = a.causal ? own0 / SW : 0;
+  const int steps = r_end + ((n - 1) / SW + 1 - c_begin);
+  auto tile_of = [&](int k) { return k < r_end ? k : c_begin + (k - r_end); };
+
+  SweepState S;
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  // Column-step statistics: threads 0..SW-1 fetch the fp64 LSE of a column
+  // step's swept rows two steps ahead and publish them to LDS one step ahead.
+  double nlt = 0.0, nls = 0.0;
+  auto fetch_stat = [&](int tile) {
+    const int g = tile * SW + tid;
+    nlt = g < n ? glt[g] : 0.0;
+    nls = g < n ? gls[g] : 0.0;
+  };
+  auto put_stat = [&](int b, int tile) {
+    const int g = tile * SW + tid;
+    float ht = 0.f, hs = 0.f, ft, fs;
+    if (g < n) {
+      split_stat(nlt, ht, ft);
+      split_stat(nls, hs, fs);
+    }
+    lstat[b][tid] = make_float2(ht, hs);
+  };
+
+  // Row steps.  The tile of the next step is copied during each step; the
+  // statistics of the first column step's rows are published after the last
+  // row step (the column steps then run their own two-ahead prefetch).
+  Tile<D, SW>::template load<NW>(lds[0][0], xt, 0, n, wave, lane);
+  Tile<D, SW>::template load<NW>(lds[0][1], xs, 0, n, wave, lane);
+  int k = 0;
+  for (; k < r_end; ++k) {
+    const int buf = k & 1, sw0 = k * SW;
+    wait_loads();
+    __syncthreads();
+    if (k + 1 < steps) {
+      const int nx = tile_of(k + 1) * SW;
+      Tile<D, SW>::template load<NW>(lds[buf ^ 1][0], xt, nx, n, wave, lane);
+      Tile<D, SW>::template load<NW>(lds[buf ^ 1][1], xs, nx, n, wave, lane);
+    }
+    const char* lt = lds[buf][0];
+    const char* ls = lds[buf][1];
+    // 32-row key blocks up to this wave's diagonal block.
+#pragma unroll
+    for (int sb = 0; sb < SW / 32; ++sb) {
+      const int swb = sw0 + 32 * sb;
+      if ((a.causal && swb > wown0 + 31) || swb >= n) break;
+      const bool need_mask = (a.causal && swb + 31 > wown0) || swb + 32 > n;
+      f32x16 St, Ss;
+      logits<D>(lt, ls, Bt, Bs, St, Ss, sb, lane);
+      if (need_mask || swb == wown0)
+        block_elementwise<ROLE_ROW, true>(St, Ss, c, swb, o, n, a.causal, h, l2t, l2s, nullptr, S);
+      else
+        block_elementwise<ROLE_ROW, false>(St, Ss, c, swb, o, n, a.causal, h, l2t, l2s, nullptr, S);
+      contract<D>(St, ls, sb, lane, acc);
+    }
+  }
+
+  // Row KL, and the diagonal term: both off-diagonal sums of dZ(k,.) stand in
+  // for -2 dZ(k,k) (see the row sweep).
+  S.kl += __shfl_xor(S.kl, 32);
+  S.dsum += __shfl_xor(S.dsum, 32);
+  const double klr = exp2(-(double)lot) * S.kl + (double)los - (double)lot;
+  if (h == 0 && o < n && a.row_kl != nullptr) a.row_kl[bh * n + o] = (float)(klr * kLn2D);
+  const float corr = (float)(-2.0 * S.dsum);
+
+  // Column steps.  No column step has run, so lstat is free.
+  if (tid < SW && k < steps) {
+    fetch_stat(tile_of(k));
+    put_stat(k & 1, tile_of(k));
+    if (k + 1 < steps) fetch_stat(tile_of(k + 1));
+  }
+  for (; k < steps; ++k) {
+    const int buf = k & 1, sw0 = tile_of(k) * SW;
+    wait_loads();
+    __syncthreads();
+    if (k + 1 < steps) {
+      const int nx = tile_of(k + 1) * SW;
+      Tile<D, SW>::template load<NW>(lds[buf ^ 1][0], xt, nx, n, wave, lane);
+      Tile<D, SW>::template load<NW>(lds[buf ^ 1][1], xs, nx, n, wave, lane);
+      if (tid < SW) {
+        put_stat(buf ^ 1, tile_of(k + 1));
+        if (k + 2 < steps) fetch_stat(tile_of(k + 2));
+      }
+    }
+    const char* lt = lds[buf][0];
+    const char* ls = lds[buf][1];
+    // Row tiles at or below the diagonal of this wave's rows (as keys).
+    if (a.causal && wown0 > sw0 + SW - 1) continue;
+    const bool need_mask = (a.causal && wown0 + 31 > sw0) || (sw0 + SW > n);
+    const bool special = need_mask || (sw0 <= wown0 + 31 && sw0 + SW - 1 >= wown0);
+#pragma unroll
+    for (int sb = 0; sb < SW / 32; ++sb) {
+      const float2* stat = &lstat[buf][32 * sb];
+      f32x16 St, Ss;
+      logits<D>(lt, ls, Bt, Bs, St, Ss, sb, lane);
+      if (special)
+        block_elementwise<ROLE_COL, true>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
+      else
+        block_elementwise<ROLE_COL, false>(St, Ss, c, sw0 + 32 * sb, o, n, a.causal, h, l2t, l2s, stat, S);
+      contract<D>(St, ls, sb, lane, acc);
+    }
+  }
+
+  const float gs = a.grad_scale;
+  if (o < n) {
+    float* dst = a.dx + (bh * (int64_t)n + o) * D;
+    const char* xo = xs + (int64_t)o * RB;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * h;
+        const uint2 raw = *reinterpret_cast<const uint2*>(xo + 2 * d0);
+        const float x4[4] = {__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                             __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(corr, x4[e], acc[db][4 * g4 + e]) * gs;
+        *reinterpret_cast<f32x4*>(dst + d0) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Deterministic fp64 reduction of row_kl to the loss scalar.
 // ---------------------------------------------------------------------------
 constexpr int kRedThreads = 256;
@@ -885,6 +1060,15 @@ hipError_t sweep_typed(const MapSet& s, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t fused_typed(const MapSet& s, hipStream_t st) {
+  constexpr int NW = LMR_W_ROW, SW = LMR_SW_ROW;
+  const int nb = blocks_per_head(s.map[0].n, NW);
+  hipLaunchKernelGGL((kl_fused_kernel<D, NW, SW>), dim3((unsigned)(nb * s.head0[s.nmaps])), dim3(64 * NW), 0, st, s,
+                     nb);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_lse_fwd(const SweepArgs& a, hipStream_t st) {
@@ -915,6 +1099,12 @@ hipError_t launch_kl_col(const SweepArgs& a, hipStream_t st) {
   if ((a.cross ? a.dy : a.dx) == nullptr) return hipSuccess;
   if (a.fp32) return launch_wide_kl_col(a, st);
   return launch_kl_col_multi(single(a), st);
+}
+
+hipError_t launch_kl_fused(const SweepArgs& a, hipStream_t st) { return launch_kl_fused_multi(single(a), st); }
+
+hipError_t launch_kl_fused_multi(const MapSet& s, hipStream_t st) {
+  return s.map[0].d == 64 ? fused_typed<64>(s, st) : fused_typed<128>(s, st);
 }
 
 hipError_t launch_lse_fwd_multi(const MapSet& s, hipStream_t st) {

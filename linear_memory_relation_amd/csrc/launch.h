@@ -48,6 +48,10 @@ hipError_t launch_kl_row(const SweepArgs& a, hipStream_t st);
 // Column-owned phase-2 sweep: adds the column term dZ^T X_s into dx (self)
 // or dy (cross).
 hipError_t launch_kl_col(const SweepArgs& a, hipStream_t st);
+// Fused phase 2 of a self-relation with gradient (bf16): row KL and the whole
+// dX_s (row and column terms) stored once; row_kl and dx required, cross == 0.
+hipError_t launch_kl_fused(const SweepArgs& a, hipStream_t st);
+hipError_t launch_kl_fused_multi(const MapSet& s, hipStream_t st);
 // fp32-input path (fp64 arithmetic on the vector ALUs), in wide.hip.
 hipError_t launch_wide_lse_fwd(const SweepArgs& a, hipStream_t st);
 hipError_t launch_wide_kl_row(const SweepArgs& a, hipStream_t st);

@@ -63,8 +63,10 @@ int main() {
          LARARD_E_INVALID);
 
   // phase 2
-  for (int mode : {0, 1, 2, 3, -7}) {
-    const int want = (mode == 0 || mode == 1) ? LARARD_OK : mode == 2 ? LARARD_E_UNSUPPORTED : LARARD_E_INVALID;
+  for (int mode : {0, 1, 2, 3, 4, -7}) {
+    const int want = (mode == 0 || mode == 1 || mode == 3) ? LARARD_OK
+                     : mode == 2                           ? LARARD_E_UNSUPPORTED
+                                                           : LARARD_E_INVALID;
     expect("kl_bwd mode", larard_kl_bwd(nullptr, nullptr, bf, 1, 1, 0, 64, 0.1f, 1, nullptr, nullptr, 1.f, nullptr,
                                         nullptr, mode, nullptr), want);
   }

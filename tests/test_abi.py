@@ -243,9 +243,9 @@ def test_proj_bwd_workspace_and_validation(lib):
     assert _proj(lib, B=0) == 1
 
 
-@pytest.mark.parametrize("mode,code", [(0, 0), (1, 0), (2, 2), (3, 1), (-1, 1)])
+@pytest.mark.parametrize("mode,code", [(0, 0), (1, 0), (3, 0), (2, 2), (4, 1), (-1, 1)])
 def test_dx_mode_status(lib, mode, code):
-    """AUTO and SPLIT are accepted; ATOMIC is not built (LARARD_E_UNSUPPORTED, before any
+    """AUTO, SPLIT and FUSED are accepted; ATOMIC is not built (LARARD_E_UNSUPPORTED, before any
     launch); anything else is invalid.  n == 0 keeps larard_kl_bwd from launching; larard_loss
     (which writes a zero loss with a kernel when n == 0) is called only with rejected modes."""
     st = lib.larard_kl_bwd(None, None, 0, 1, 1, 0, 64, 0.1, 1, None, None, 1.0, None, None, mode, None)

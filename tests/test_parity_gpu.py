@@ -78,13 +78,19 @@ def test_tiny_fp32_rope_pi4(gpu_lib):
     _compare(got, ref, "f32", w.n, _logit_bound(m.xt64, m.xs64, w.scale))
 
 
+# Phase-2 modes of the bf16 path: FUSED (one sweep per row block) and SPLIT
+# (row sweep, then column sweep; AUTO's choice).
+MODES = [pytest.param(3, id="fused"), pytest.param(1, id="split")]
+
+
 # Lengths around the 32-row block, the 128-row tile and the 256-row workgroup.
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("n", [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 333, 511, 513])
 @pytest.mark.parametrize("d", [64, 128])
-def test_bf16_ragged_lengths(gpu_lib, n, d):
+def test_bf16_ragged_lengths(gpu_lib, n, d, mode):
     xt, xs = random_pair(1, 2, n, d, 0.4, seed=n * 7 + d)
     s = 1.0 / np.sqrt(d)
-    got = _run(gpu_lib, xt, xs, "bf16", s)
+    got = _run(gpu_lib, xt, xs, "bf16", s, dx_mode=mode)
     a, b = widen(xt, "bf16"), widen(xs, "bf16")
     ref = oracle.relation_kl(a, b, f32(s), True)
     _compare(got, ref, "bf16", n, _logit_bound(a, b, s), scale=s, xmax=float(np.max(np.abs(b))))
@@ -101,12 +107,13 @@ def test_fp32_ragged_lengths(gpu_lib, n, d):
     _compare(got, ref, "f32", n, _logit_bound(a, b, s))
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("n,d,dtype", [(200, 128, "bf16"), (129, 64, "bf16"), (100, 64, "f32"), (257, 64, "bf16"),
                                          (513, 128, "bf16")])
-def test_bidirectional_mask(gpu_lib, n, d, dtype):
+def test_bidirectional_mask(gpu_lib, n, d, dtype, mode):
     xt, xs = random_pair(1, 3, n, d, 0.5, seed=5, dtype=dtype)
     s = 1.0 / np.sqrt(d)
-    got = _run(gpu_lib, xt, xs, dtype, s, causal=False)
+    got = _run(gpu_lib, xt, xs, dtype, s, causal=False, dx_mode=mode)
     a, b = widen(xt, dtype), widen(xs, dtype)
     ref = oracle.relation_kl(a, b, f32(s), False)
     _compare(got, ref, dtype, n, _logit_bound(a, b, s))
@@ -251,17 +258,36 @@ def test_kl_fwd_peaky_heads(gpu_lib):
     _fwd_compare(*got, ref, "bf16", _logit_bound(a, b, w.scale))
 
 
-def test_split_mode_is_bitwise_deterministic(gpu_lib):
+@pytest.mark.parametrize("mode", MODES)
+def test_phase2_modes_are_bitwise_deterministic(gpu_lib, mode):
     import torch
     xt, xs = random_pair(1, 4, 700, 128, 0.3, seed=6)
     a, b = to_device(xt, "bf16"), to_device(xs, "bf16")
     outs = []
     for _ in range(3):
-        loss, dx = gpu_lib.loss(a, b, dx_mode=gpu_lib.DX_SPLIT)
+        loss, dx = gpu_lib.loss(a, b, dx_mode=mode)
         torch.cuda.synchronize()
         outs.append((float(loss.cpu()), dx.cpu().numpy()))
     for o in outs[1:]:
         assert o[0] == outs[0][0] and np.array_equal(o[1], outs[0][1])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fused_and_split_agree(gpu_lib, causal):
+    """The two phase-2 modes add the same terms in different orders: the row KL
+    and loss are bit for bit the same (same row sweep arithmetic), the gradient
+    agrees to fp32 rounding."""
+    import torch
+    xt, xs = random_pair(2, 3, 611, 128, 0.3, seed=21)
+    a, b = to_device(xt, "bf16"), to_device(xs, "bf16")
+    lt, ls = gpu_lib.lse_fwd(a, b, None, causal)
+    kf, df = gpu_lib.kl_bwd(a, b, lt, ls, None, causal, dx_mode=gpu_lib.DX_FUSED)
+    ks, ds = gpu_lib.kl_bwd(a, b, lt, ls, None, causal, dx_mode=gpu_lib.DX_SPLIT)
+    torch.cuda.synchronize()
+    assert torch.equal(kf, ks)
+    e = float((df - ds).abs().max() / ds.abs().max())
+    print(f"  fused vs split (causal={causal}): normwise max difference {e:.2e}", flush=True)
+    assert e < 1e-5
 
 
 @pytest.mark.parametrize("causal", [True, False])
