@@ -83,6 +83,27 @@ enum : int { ROLE_ROW = 0, ROLE_COL = 1 };
 #ifndef LMR_LSE_OCC
 #define LMR_LSE_OCC 2
 #endif
+// Phase 1 also comes in a wide shape: 12 waves (384 owned rows) sweeping
+// 96-row tiles in 96 KiB of LDS.  It fits 3 waves per SIMD in its registers
+// (the 8-wave shape's 128 KiB of LDS allows only 2), which measured 4% faster
+// at n = 16K, but its larger row blocks leave small grids with a long tail,
+// so it is used only when its grid has at least LMR_LSE_WIDE_MIN_GRID
+// workgroups.
+#ifndef LMR_W_LSE_WIDE
+#define LMR_W_LSE_WIDE 12
+#endif
+#ifndef LMR_SW_LSE_WIDE
+#define LMR_SW_LSE_WIDE 96
+#endif
+#ifndef LMR_LSE_WIDE_MIN_GRID
+#define LMR_LSE_WIDE_MIN_GRID 1024
+#endif
+// Whether the forward-only sweep (phase 1 with the KL accumulator) takes the
+// wide shape too.  Off: its extra accumulator spills at 3 waves per SIMD, and
+// the 8-wave shape measured 2% faster at n = 16K and 8K.
+#ifndef LMR_LSE_WIDE_KL
+#define LMR_LSE_WIDE_KL 0
+#endif
 
 __device__ inline f32x16 mma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -1038,10 +1059,18 @@ MapSet single(const SweepArgs& a) {
 
 template <int D, bool KL>
 hipError_t lse_typed(const MapSet& s, hipStream_t st) {
-  constexpr int NW = LMR_W_LSE;
-  const int nb = blocks_per_head(s.map[0].n, NW);
-  hipLaunchKernelGGL((lse_fwd_kernel<D, KL, NW, LMR_SW_LSE>), dim3((unsigned)(nb * s.head0[s.nmaps])), dim3(64 * NW),
-                     0, st, s, nb);
+  const int64_t heads = s.head0[s.nmaps];
+  const int nbw = blocks_per_head(s.map[0].n, LMR_W_LSE_WIDE);
+  if ((!KL || LMR_LSE_WIDE_KL) && (int64_t)nbw * heads >= LMR_LSE_WIDE_MIN_GRID) {
+    constexpr int NW = LMR_W_LSE_WIDE;
+    hipLaunchKernelGGL((lse_fwd_kernel<D, KL, NW, LMR_SW_LSE_WIDE>), dim3((unsigned)(nbw * heads)), dim3(64 * NW), 0,
+                       st, s, nbw);
+  } else {
+    constexpr int NW = LMR_W_LSE;
+    const int nb = blocks_per_head(s.map[0].n, NW);
+    hipLaunchKernelGGL((lse_fwd_kernel<D, KL, NW, LMR_SW_LSE>), dim3((unsigned)(nb * heads)), dim3(64 * NW), 0, st,
+                       s, nb);
+  }
   return hipGetLastError();
 }
 

@@ -306,3 +306,72 @@ def test_overflowing_shift_takes_the_exact_fallback(gpu_lib, causal):
     ref = oracle.relation_kl(a, b, 0.125, causal)
     assert np.all(np.isfinite(got["lse_t"])) and np.all(np.isfinite(got["dx"]))
     _compare(got, ref, "bf16", n, _logit_bound(a, b, 0.125))
+
+
+# Phase 1 switches to its wide shape (12 waves, 384-row blocks, 96-row key
+# tiles) when that grid has at least 1024 workgroups.  Many heads at ragged
+# lengths reach it at small n; sampled heads are checked against the oracle.
+WIDE_GRID = 1024
+
+
+def _wide_heads(n):
+    """Head count (B = 2) whose wide phase-1 grid reaches WIDE_GRID."""
+    blocks = -(-n // 384)
+    return -(-WIDE_GRID // (2 * blocks))
+
+
+@pytest.mark.parametrize("n,d", [(385, 128), (500, 64), (777, 128), (1152, 128)])
+def test_wide_phase1_shape(gpu_lib, n, d):
+    import torch
+    H = _wide_heads(n)
+    xt, xs = random_pair(2, H, n, d, 0.4, seed=n + d)
+    s = 1.0 / np.sqrt(d)
+    a, b = to_device(xt, "bf16"), to_device(xs, "bf16")
+    ws = torch.empty(gpu_lib.workspace_bytes(2, H, n), dtype=torch.uint8, device="cuda")
+    loss, dx = gpu_lib.loss(a, b, s, True, workspace=ws)
+    f_lt, f_ls, f_kl = gpu_lib.kl_fwd(a, b, s, True)
+    torch.cuda.synchronize()
+    off = gpu_lib.workspace_layout(2, H, n)
+    lse_t = ws[off[0]:off[0] + 8 * 2 * H * n].view(torch.float64).view(2, H, n).cpu().numpy()
+    row_kl = ws[off[2]:off[2] + 4 * 2 * H * n].view(torch.float32).view(2, H, n).cpu().numpy()
+    assert np.array_equal(f_lt.cpu().numpy(), lse_t)            # same sums, same order
+    rng = np.random.default_rng(n)
+    for bb, hh in [(0, 0), (1, H - 1), (int(rng.integers(2)), int(rng.integers(H)))]:
+        xa, xb = widen(xt[bb, hh], "bf16"), widen(xs[bb, hh], "bf16")
+        ref = oracle.relation_kl_head(xa, xb, f32(s), True)
+        zmax = _logit_bound(xa, xb, s)
+        assert np.max(np.abs(lse_t[bb, hh] - ref["lse_t"])) < 2e-6 * (1 + np.max(np.abs(ref["lse_t"]))) + 8 * EPS32 * zmax
+        kl_tol = 2e-6 + 1e-4 * np.max(np.abs(ref["row_kl"])) + 8 * EPS32 * zmax
+        assert np.max(np.abs(row_kl[bb, hh] - ref["row_kl"])) < kl_tol
+        assert np.max(np.abs(f_kl[bb, hh].cpu().numpy() - ref["row_kl"])) < kl_tol
+        assert normwise_max_rel(dx[bb, hh].cpu().numpy(), ref["dself"]) < 2e-2
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_wide_phase1_overflow_fallback(gpu_lib, causal):
+    """Huge-norm rows in some heads make the fixed shift overflow: those 384-row
+    blocks of the wide phase 1 redo their rows with the online maximum."""
+    import torch
+    n, d = 450, 64
+    H = _wide_heads(n)
+    rng = np.random.default_rng(21)
+    xt = rng.standard_normal((2, H, n, d))
+    xt[:, ::37, 3] *= 30.0
+    xt[:, ::53, 400] *= 30.0
+    xs = xt + 0.3 * rng.standard_normal(xt.shape)
+    xt, xs = si.round_bf16_bits(xt), si.round_bf16_bits(xs)
+    a, b = to_device(xt, "bf16"), to_device(xs, "bf16")
+    lt, ls = gpu_lib.lse_fwd(a, b, 0.125, causal)
+    f_lt, f_ls, f_kl = gpu_lib.kl_fwd(a, b, 0.125, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(lt, f_lt) and torch.equal(ls, f_ls)
+    for bb, hh in [(0, 0), (1, 37), (0, 53), (1, 106)]:
+        xa, xb = widen(xt[bb, hh], "bf16"), widen(xs[bb, hh], "bf16")
+        ref = oracle.relation_kl_head(xa, xb, 0.125, causal)
+        zmax = _logit_bound(xa, xb, 0.125)
+        for got, want in ((lt, ref["lse_t"]), (ls, ref["lse_s"])):
+            g = got[bb, hh].cpu().numpy()
+            assert np.all(np.isfinite(g))
+            assert np.max(np.abs(g - want)) < 2e-6 * (1 + np.max(np.abs(want))) + 8 * EPS32 * zmax
+        kl_tol = 2e-6 + 1e-4 * np.max(np.abs(ref["row_kl"])) + 8 * EPS32 * zmax
+        assert np.max(np.abs(f_kl[bb, hh].cpu().numpy() - ref["row_kl"])) < kl_tol
