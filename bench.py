@@ -600,8 +600,20 @@ def extra_workload(name, args, dev):
     torch.cuda.synchronize()
     free_after_alloc = torch.cuda.mem_get_info()[0]
     torch.cuda.reset_peak_memory_stats()
-    ms, per_kernel, _, _ = run_steps(bufs, w.scale, args.extra_steps, 1)
+    # AUTO's phase-2 mode for this length (fused up to n = 8192, as larard_kl_bwd
+    # decides), and the other mode beside it.
+    mode = "fused" if w.n <= 8192 else "split"
+    other = "split" if mode == "fused" else "fused"
+    # Per-kernel times from one evented run; the two modes' step times from
+    # event-free runs in alternation (A B A B), so that neither mode pays the
+    # events or the first-run warm-up alone.
+    _, per_kernel, _, _ = run_steps(bufs, w.scale, args.extra_steps, 2, mode=mode)
     free_after_steps = torch.cuda.mem_get_info()[0]
+    t = {mode: [], other: []}
+    for _ in range(2):
+        for m in (mode, other):
+            t[m].append(run_steps(bufs, w.scale, args.extra_steps, 1, events=False, mode=m)[0])
+    ms, ms_other = float(np.mean(t[mode])), float(np.mean(t[other]))
     peak = torch.cuda.max_memory_allocated() - base_alloc
     memory = memory_report(bufs, base_alloc, peak, free_before, free_after_alloc, free_after_steps)
     flops = sum(6 * units(b) for b in bufs)
@@ -610,6 +622,7 @@ def extra_workload(name, args, dev):
            "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
            "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
            "kernels_avg_ms": {k: round(float(np.mean(v)), 4) for k, v in per_kernel.items()},
+           "phase2_mode": mode, f"ms_per_step_{other}_phase2": round(ms_other, 4),
            "fused_maps_ms_per_step": round(ms_maps, 4),
            "losses": {b["name"]: float(b["loss"].cpu()) for b in bufs},
            "memory": memory}

@@ -89,9 +89,11 @@ typedef enum {
  *           workgroups -- 8.6 GB at n = 16K, H = 32 -- and coalesced fp32
  *           atomic adds sustain ~1.4 TB/s on MI355X, longer than the
  *           split's whole second sweep.)
- *   AUTO  : SPLIT, measured faster than FUSED on MI355X (16K: 6.29 against
- *           6.60 ms per 32-head map), although FUSED moves a third less HBM
- *           traffic.
+ *   AUTO  : FUSED for n <= 8192, SPLIT above, by measurement on MI355X:
+ *           FUSED is 3% faster per step at n = 4K and 2% at 8K, where the
+ *           split sweeps' causal tails show, and 1.4% slower at 16K, although
+ *           it moves a third less HBM traffic.  (larard_multi_loss follows
+ *           the same rule.)
  * FUSED and SPLIT execute the same contractions (phase 2 computes every
  * logit tile twice) and give the same results to fp32 rounding; each is
  * bitwise reproducible. */

@@ -334,7 +334,9 @@ def test_wide_phase1_shape(gpu_lib, n, d):
     off = gpu_lib.workspace_layout(2, H, n)
     lse_t = ws[off[0]:off[0] + 8 * 2 * H * n].view(torch.float64).view(2, H, n).cpu().numpy()
     row_kl = ws[off[2]:off[2] + 4 * 2 * H * n].view(torch.float32).view(2, H, n).cpu().numpy()
-    assert np.array_equal(f_lt.cpu().numpy(), lse_t)            # same sums, same order
+    # Every row's sum runs over the same 32-row blocks in the same order in
+    # either phase-1 shape, so the forward-only sweep's LSE is bit-equal.
+    assert np.array_equal(f_lt.cpu().numpy(), lse_t)
     rng = np.random.default_rng(n)
     for bb, hh in [(0, 0), (1, H - 1), (int(rng.integers(2)), int(rng.integers(H)))]:
         xa, xb = widen(xt[bb, hh], "bf16"), widen(xs[bb, hh], "bf16")
@@ -364,14 +366,31 @@ def test_wide_phase1_overflow_fallback(gpu_lib, causal):
     lt, ls = gpu_lib.lse_fwd(a, b, 0.125, causal)
     f_lt, f_ls, f_kl = gpu_lib.kl_fwd(a, b, 0.125, causal)
     torch.cuda.synchronize()
-    assert torch.equal(lt, f_lt) and torch.equal(ls, f_ls)
+    # (The forward-only sweep keeps 256-row blocks, so its fallback re-sums
+    # other sets of rows with the online maximum: both exact, not bit-equal.)
     for bb, hh in [(0, 0), (1, 37), (0, 53), (1, 106)]:
         xa, xb = widen(xt[bb, hh], "bf16"), widen(xs[bb, hh], "bf16")
         ref = oracle.relation_kl_head(xa, xb, 0.125, causal)
         zmax = _logit_bound(xa, xb, 0.125)
-        for got, want in ((lt, ref["lse_t"]), (ls, ref["lse_s"])):
+        for got, want in ((lt, ref["lse_t"]), (ls, ref["lse_s"]), (f_lt, ref["lse_t"]), (f_ls, ref["lse_s"])):
             g = got[bb, hh].cpu().numpy()
             assert np.all(np.isfinite(g))
             assert np.max(np.abs(g - want)) < 2e-6 * (1 + np.max(np.abs(want))) + 8 * EPS32 * zmax
         kl_tol = 2e-6 + 1e-4 * np.max(np.abs(ref["row_kl"])) + 8 * EPS32 * zmax
         assert np.max(np.abs(f_kl[bb, hh].cpu().numpy() - ref["row_kl"])) < kl_tol
+
+
+@pytest.mark.parametrize("n,expect", [(8192, 3), (8193, 1)])
+def test_auto_mode_choice(gpu_lib, n, expect):
+    """AUTO runs the fused phase 2 up to n = 8192 and the split sweeps above:
+    its gradient equals that mode's bit for bit (the two modes differ in the
+    last bits)."""
+    import torch
+    xt, xs = random_pair(1, 1, n, 64, 0.3, seed=n)
+    a, b = to_device(xt, "bf16"), to_device(xs, "bf16")
+    _, d_auto = gpu_lib.loss(a, b, dx_mode=gpu_lib.DX_AUTO)
+    _, d_want = gpu_lib.loss(a, b, dx_mode=expect)
+    _, d_other = gpu_lib.loss(a, b, dx_mode=4 - expect if expect == 3 else 3)
+    torch.cuda.synchronize()
+    assert torch.equal(d_auto, d_want)
+    assert not torch.equal(d_auto, d_other)
