@@ -586,6 +586,35 @@ def time_fused_maps(bufs, scale, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
+def reference_gemm(dev, reps: int = 200, size: int = 8192):
+    """The vendor library's dense bf16 GEMM (torch.matmul, hipBLASLt underneath) on random normal
+    operands, timed over enough repetitions to reach the clock the GPU sustains under MFMA load.
+    It is a measured reference for what a plain MFMA contraction reaches on this GPU, beside the
+    nominal peak; the relation-KL step's figures stay priced against the nominal peak."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    a = torch.randn(size, size, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(size, size, device=dev, dtype=torch.bfloat16, generator=g)
+    c = torch.empty(size, size, device=dev, dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    tflops = 2.0 * size ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"what": "torch.matmul bf16 x bf16 -> bf16 (fp32 accumulate), random normal operands",
+            "shape_mnk": [size, size, size], "reps": reps, "ms": round(ms, 4), "tflops": round(tflops, 1),
+            "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
 def extra_workload(name, args, dev):
     """ms/step, TFLOP/s and memory of one more workload, timed like the headline one."""
     import gc
@@ -744,6 +773,10 @@ def main():
     torch.cuda.empty_cache()
     for name in [x for x in args.extra_workloads.split(",") if x and x != w.name]:
         extra[name] = extra_workload(name, args, dev)
+    gemm_ref = None
+    if not args.core_only:
+        gemm_ref = reference_gemm(dev)
+        gemm_ref["step_value_over_gemm"] = round(value / gemm_ref["tflops"], 4)
 
     out = {
         "metric": "relation-KL fwd+bwd ms/step & TFLOP/s (% bf16 MFMA peak) at H=32,d=128,n=16K",
@@ -774,6 +807,7 @@ def main():
         "cross_relation": cross,
         "proj_bwd": proj,
         "fused_maps": fused_info,
+        "reference_gemm": gemm_ref,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, maps, args.cpu_sample_n)
