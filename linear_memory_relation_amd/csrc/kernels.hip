@@ -394,7 +394,7 @@ __device__ inline void lse_finish(const SweepArgs& a, int64_t bh, const char* yt
     Tile<D, SW>::template load<NW>(lds[buf][1], ys, sw0, n, wave, lane);
     wait_loads();
     __syncthreads();
-    if (a.causal && sw0 > wown0 + 31) continue;
+    if (wown0 >= n || (a.causal && sw0 > wown0 + 31)) continue;
 #pragma unroll
     for (int sb = 0; sb < SW / 32; ++sb) {
       f32x16 St, Ss;
@@ -430,7 +430,7 @@ __device__ inline void lse_finish(const SweepArgs& a, int64_t bh, const char* yt
     Tile<D, SW>::template load<NW>(lds[buf][1], ys, sw0, n, wave, lane);
     wait_loads();
     __syncthreads();
-    if (a.causal && sw0 > wown0 + 31) continue;
+    if (wown0 >= n || (a.causal && sw0 > wown0 + 31)) continue;
 #pragma unroll
     for (int sb = 0; sb < SW / 32; ++sb) {
       f32x16 St, Ss;
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(64 * NW, LMR_LSE_OCC) void lse_fwd_kernel(MapSet ma
     for (int sb = 0; sb < SW / 32; ++sb) {
       // 32-row block: stop past this wave's diagonal block or past the end.
       const int swb = sw0 + 32 * sb;
-      if ((a.causal && swb > wown0 + 31) || swb >= n) break;
+      if (wown0 >= n || (a.causal && swb > wown0 + 31) || swb >= n) break;
       const bool need_mask = (a.causal && swb + 31 > wown0) || swb + 32 > n;
       f32x16 St, Ss;
       logits<D>(lds[buf][0], lds[buf][1], Bt, Bs, St, Ss, sb, lane);
@@ -734,7 +734,7 @@ __global__ __launch_bounds__(64 * NW, LMR_SWEEP_OCC) void kl_sweep_kernel(MapSet
       }
     } else {
       // Column sweep: decided per tile (per-block tests measured slower here).
-      if (a.causal && wown0 > sw0 + SW - 1) continue;        // tile entirely above the diagonal
+      if (wown0 >= n || (a.causal && wown0 > sw0 + SW - 1)) continue;        // tile entirely above the diagonal
       const bool need_mask = (a.causal && wown0 + 31 > sw0) || (sw0 + SW > n);
       // Tiles that hold a diagonal entry of this wave take the per-entry path too.
       const bool special = need_mask || (sw0 <= wown0 + 31 && sw0 + SW - 1 >= wown0);
@@ -915,7 +915,7 @@ __global__ __launch_bounds__(64 * NW, LMR_SWEEP_OCC) void kl_fused_kernel(MapSet
 #pragma unroll
     for (int sb = 0; sb < SW / 32; ++sb) {
       const int swb = sw0 + 32 * sb;
-      if ((a.causal && swb > wown0 + 31) || swb >= n) break;
+      if (wown0 >= n || (a.causal && swb > wown0 + 31) || swb >= n) break;
       const bool need_mask = (a.causal && swb + 31 > wown0) || swb + 32 > n;
       f32x16 St, Ss;
       logits<D>(lt, ls, Bt, Bs, St, Ss, sb, lane);
@@ -957,7 +957,7 @@ __global__ __launch_bounds__(64 * NW, LMR_SWEEP_OCC) void kl_fused_kernel(MapSet
     const char* lt = lds[buf][0];
     const char* ls = lds[buf][1];
     // Row tiles at or below the diagonal of this wave's rows (as keys).
-    if (a.causal && wown0 > sw0 + SW - 1) continue;
+    if (wown0 >= n || (a.causal && wown0 > sw0 + SW - 1)) continue;
     const bool need_mask = (a.causal && wown0 + 31 > sw0) || (sw0 + SW > n);
     const bool special = need_mask || (sw0 <= wown0 + 31 && sw0 + SW - 1 >= wown0);
 #pragma unroll
