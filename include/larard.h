@@ -307,7 +307,10 @@ larard_status larard_multi_loss(const larard_map* maps, int n_maps, larard_dtype
  * NULL; dw: fp32 [dm, H*d], OVERWRITTEN.  R^T dX_s is rounded to bf16 and
  * contracted on bf16 MFMA with fp32 accumulation.  dm and H*d must be
  * multiples of 128 (LARARD_E_UNSUPPORTED otherwise), d 64 or 128.  The
- * workspace (device, 256-byte aligned) holds the K-major bf16 operands.
+ * workspace (device, 256-byte aligned) holds (R^T dX_s)^T in bf16,
+ * [H*d, B*n rounded up to 64], and for large outputs (dm and H*d multiples
+ * of 256 with (dm/256)*(H*d/256) >= 256) h^T [dm, B*n rounded up to 64] as
+ * well; smaller outputs read h in place.
  * ------------------------------------------------------------------------- */
 size_t larard_proj_bwd_workspace_bytes(int64_t B, int64_t n, int64_t dm, int64_t H, int64_t d);
 

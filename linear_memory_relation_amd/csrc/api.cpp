@@ -597,7 +597,8 @@ int64_t proj_kp(int64_t B, int64_t n) { return (B * n + 63) / 64 * 64; }
 size_t larard_proj_bwd_workspace_bytes(int64_t B, int64_t n, int64_t dm, int64_t H, int64_t d) {
   if (!proj_sizes_ok(B, n, dm, H, d)) return 0;
   const size_t kp = (size_t)proj_kp(B, n);
-  return align256((size_t)(H * d) * kp * 2) + align256((size_t)dm * kp * 2);
+  const size_t g = align256((size_t)(H * d) * kp * 2);
+  return lmr::proj_uses_256_tiles(dm, H * d) ? g + align256((size_t)dm * kp * 2) : g;
 }
 
 larard_status larard_proj_bwd(const void* h, const float* dx_s, int64_t B, int64_t n, int64_t dm, int64_t H,
@@ -633,8 +634,10 @@ larard_status larard_proj_bwd(const void* h, const float* dx_s, int64_t B, int64
   p.H = H;
   p.d = d;
   p.kp = proj_kp(B, n);
-  p.gt = static_cast<uint16_t*>(workspace);
-  p.ht = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + align256((size_t)(H * d) * (size_t)p.kp * 2));
+  p.g = static_cast<uint16_t*>(workspace);
+  p.ht = lmr::proj_uses_256_tiles(dm, H * d)
+             ? reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + align256((size_t)(H * d) * (size_t)p.kp * 2))
+             : nullptr;
   p.dw = dw;
   const hipError_t e = lmr::launch_proj_bwd(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LARARD_OK : hip_fail(e, "proj_bwd launch");

@@ -77,13 +77,16 @@ struct ProjArgs {
   const float* dx;       // [B, H, n, d] fp32 student gradient
   const float* cos;      // [n, d/2] fp32 student rotation tables (null: no rotation)
   const float* sin;
-  uint16_t* gt;          // workspace: G^T [H*d, kp] bf16
-  uint16_t* ht;          // workspace: h^T [dm, kp] bf16
+  uint16_t* g;           // workspace: G^T = (R^T dX_s)^T [H*d, kp] bf16 (tokens permuted per 16)
+  uint16_t* ht;          // workspace: h^T [dm, kp] bf16, same token order (256-tile path only)
   float* dw;             // [dm, H*d] fp32 output
   int64_t B, n, dm, H, d;
   int64_t kp;            // B*n rounded up to a multiple of 64
 };
 hipError_t launch_proj_bwd(const ProjArgs& p, hipStream_t st);
+// Whether launch_proj_bwd takes the 256 x 256 tile path, which also needs
+// the h^T workspace region.
+bool proj_uses_256_tiles(int64_t dm, int64_t hd);
 
 // *loss = 0 (used when n == 0).
 hipError_t launch_zero_scalar(float* loss, hipStream_t st);

@@ -229,7 +229,11 @@ def _proj(lib, **kw):
 def test_proj_bwd_workspace_and_validation(lib):
     kp = (2 * 100 + 63) // 64 * 64
     up = lambda v: (v + 255) // 256 * 256
-    assert lib.larard_proj_bwd_workspace_bytes(2, 100, 256, 2, 128) == up(256 * kp * 2) + up(256 * kp * 2)
+    # (R^T dX_s)^T in bf16, [H*d, kp]; small outputs read h in place
+    assert lib.larard_proj_bwd_workspace_bytes(2, 100, 256, 2, 128) == up(2 * 128 * kp * 2)
+    # 256 x 256 output tiles (dm = H*d = 4096): h^T [dm, kp] as well
+    assert lib.larard_proj_bwd_workspace_bytes(1, 4096, 4096, 32, 128) == 2 * 4096 * 4096 * 2
+    assert lib.larard_proj_bwd_workspace_bytes(2, 8192, 4096, 8, 128) == 1024 * 16384 * 2
     assert lib.larard_proj_bwd_workspace_bytes(1, 100, 200, 2, 128) == 0       # dm not a multiple of 128
     assert _proj(lib, dm=192) == 2
     assert _proj(lib, H=1, d=64) == 2                                          # H*d = 64
