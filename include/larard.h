@@ -265,7 +265,12 @@ larard_status larard_xy_loss(const void* x_t, const void* x_s, const void* y_t, 
  * runs once over the heads of all maps, saving the launch gaps and the
  * drained tail between per-map launches.  Work is ordered map by map (map 0
  * first), and within a map by row-block length (longest first) and then by
- * head.
+ * head.  Exception: with split phase 2 (n > 8192) and every map large enough
+ * to fill the GPU alone (B * H_m * ceil(n/256) >= 1024), the maps run one
+ * after another, each through its own three sweeps, which keeps a map's
+ * projections in the last-level cache between its sweeps (5% faster phase 2
+ * at n = 16K, three maps of 32 heads, on MI355X).  Results are the same
+ * bits either way.
  * ------------------------------------------------------------------------- */
 typedef struct {
   const void* x_t;   /* [B, H, n, d] teacher projections of this map (device) */
