@@ -246,12 +246,14 @@ def summarize(trace_dir: str, copy_mib: str, pmc_dirs, cmds: str) -> str:
     valu = by_kind("SQ_ACTIVE_INST_VALU")
     coex = by_kind("SQ_VALU_MFMA_COEXEC_CYCLES")
     if gui and busy:
-        import linear_memory_relation_amd  # noqa: F401  (version printed above)
+        import linear_memory_relation_amd as lmr
         from synth_inputs import WORKLOADS
         w = WORKLOADS["llama2_16k"]
-        unit = 32 * 2 * w.d * causal_pairs(w.n)      # one GEMM-unit over the 32 heads of one map
+        hpl = lmr.loss_head_group(w.B, 32, w.n, w.d)   # heads per launch: one head group of one map
+        unit = hpl * 2 * w.d * causal_pairs(w.n)      # one GEMM-unit over the heads of one launch
         lines += ["", "## MFMA and VALU utilisation (rocprofv3 --pmc, one dispatch at a time)", ""]
-        lines += ["Per sweep kernel, mean over its dispatches (one per map):",
+        lines += [f"Per sweep kernel, mean over its dispatches (one per head group of {hpl} heads of a map; "
+                  "the step runs phase 1 and phase 2 group by group):",
                   "- `clock` = GRBM_GUI_ACTIVE per XCD / kernel-trace average duration;",
                   "- `MFMA busy` = sum of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs) "
                   "(AMD's MfmaUtil expression);",
@@ -480,7 +482,27 @@ def make_buffers(w, dev):
             partials=torch.empty((B * H,), dtype=torch.float64, device=dev),
             dx=torch.empty((B, H, n, d), dtype=torch.float32, device=dev),
             loss=torch.empty((), dtype=torch.float32, device=dev)))
+    for b in bufs:
+        b["groups"] = head_groups(b)
     return maps, bufs
+
+
+def head_groups(b):
+    """Views of one map's tensors per head group, as larard_loss schedules them: phase 1 and
+    phase 2 run for heads [h0, h0+g) of the flattened B*H heads before the next group
+    (larard_loss_head_group), so that the group's projections stay in the last-level cache."""
+    import linear_memory_relation_amd as lmr
+    bh, n, d = b["B"] * b["H"], b["n"], b["d"]
+    g = lmr.loss_head_group(b["B"], b["H"], n, d)
+    out = []
+    for h0 in range(0, bh, g):
+        c = min(g, bh - h0)
+
+        def sl(t, tail):
+            return t.reshape(1, bh, *tail)[:, h0:h0 + c]
+        out.append(dict(heads=c, xt=sl(b["xt"], (n, d)), xs=sl(b["xs"], (n, d)), lse_t=sl(b["lse_t"], (n,)),
+                        lse_s=sl(b["lse_s"], (n,)), row_kl=sl(b["row_kl"], (n,)), dx=sl(b["dx"], (n, d))))
+    return out
 
 
 # Kernels of one map's step in each phase-2 mode (the events bracket each).
@@ -494,41 +516,48 @@ EXE = {"lse_fwd": 2, "kl_bwd": 6, "kl_rows": 3, "kl_cols": 3, "reduce": 0}
 
 
 def run_steps(bufs, scale, steps, warmup, events=True, mode="split"):
-    """Warm up, then time `steps` steps (each map: phase 1, phase 2 -- one fused sweep, or the
-    row and column sweeps in split mode -- and the loss reduction, as larard_loss launches them)
-    with HIP events on the launch stream.  Returns (ms per step, per-kernel times in ms,
-    total ms, wall seconds of the timed region)."""
+    """Warm up, then time `steps` steps: each map, head group by head group (head_groups), runs
+    phase 1 and phase 2 -- one fused sweep, or the row and column sweeps in split mode -- and then
+    the map's loss reduction, as larard_loss launches them, with HIP events on the launch stream
+    around every launch.  Returns (ms per step, per-kernel launch times in ms, total ms, wall
+    seconds of the timed region); per-kernel entries are (ms, heads of the launch)."""
     import torch
     import linear_memory_relation_amd as lmr
-    kinds = KINDS[mode]
+    phases = KINDS[mode][:-1]
+    plan = []                      # kinds of one step's launches, in order, with their head counts
+    for b in bufs:
+        for grp in b["groups"]:
+            plan += [(k, grp["heads"]) for k in phases]
+        plan.append(("reduce", b["B"] * b["H"]))
 
     def step(ev=None):
-        for b in bufs:
-            a = (b["xt"], b["xs"])
-            marks = iter(ev[b["name"]]) if ev is not None else None
+        marks = iter(ev) if ev is not None else None
 
-            def mark():
-                if marks is not None:
-                    next(marks).record()
-            mark()
-            lmr.lse_fwd(*a, scale, True, b["lse_t"], b["lse_s"])
-            mark()
-            if mode == "fused":
-                lmr.kl_bwd(*a, b["lse_t"], b["lse_s"], scale, True, 1.0, dx_mode=lmr.DX_FUSED,
-                           row_kl=b["row_kl"], dx=b["dx"])
-            else:
-                lmr.kl_bwd_rows(*a, b["lse_t"], b["lse_s"], b["row_kl"], b["dx"], scale, True, 1.0)
+        def mark():
+            if marks is not None:
+                next(marks).record()
+        mark()
+        for b in bufs:
+            for grp in b["groups"]:
+                a = (grp["xt"], grp["xs"])
+                lmr.lse_fwd(*a, scale, True, grp["lse_t"], grp["lse_s"])
                 mark()
-                lmr.kl_bwd_cols(*a, b["lse_t"], b["lse_s"], b["dx"], scale, True, 1.0)
-            mark()
+                if mode == "fused":
+                    lmr.kl_bwd(*a, grp["lse_t"], grp["lse_s"], scale, True, 1.0, dx_mode=lmr.DX_FUSED,
+                               row_kl=grp["row_kl"], dx=grp["dx"])
+                else:
+                    lmr.kl_bwd_rows(*a, grp["lse_t"], grp["lse_s"], grp["row_kl"], grp["dx"], scale, True, 1.0)
+                    mark()
+                    lmr.kl_bwd_cols(*a, grp["lse_t"], grp["lse_s"], grp["dx"], scale, True, 1.0)
+                mark()
             lmr.reduce_loss(b["row_kl"], b["partials"], b["loss"], 1.0)
             mark()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [{b["name"]: [torch.cuda.Event(enable_timing=True) for _ in range(len(kinds) + 1)] for b in bufs}
-          for _ in range(steps)] if events else [None] * steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(plan) + 1)] for _ in range(steps)] \
+        if events else [None] * steps
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -539,19 +568,28 @@ def run_steps(bufs, scale, steps, warmup, events=True, mode="split"):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
-    per_kernel = {k: [] for k in kinds}
+    per_kernel = {k: [] for k in KINDS[mode]}
     if events:
         for k in range(steps):
-            for b in bufs:
-                e = ev[k][b["name"]]
-                for j, kind in enumerate(kinds):
-                    per_kernel[kind].append(e[j].elapsed_time(e[j + 1]))
+            e = ev[k]
+            for j, (kind, heads) in enumerate(plan):
+                per_kernel[kind].append((e[j].elapsed_time(e[j + 1]), heads))
     return total_ms / steps, per_kernel, total_ms, wall
+
+
+def kernel_ms(per_kernel):
+    """Mean launch time (ms) per kernel kind."""
+    return {k: float(np.mean([t for t, _ in v])) for k, v in per_kernel.items() if v}
 
 
 def units(b):
     """One GEMM-unit of a map: 2*d flop per kept pair, over all its heads."""
-    return b["B"] * b["H"] * 2 * b["d"] * causal_pairs(b["n"])
+    return b["B"] * b["H"] * units_per_head(b)
+
+
+def units_per_head(b):
+    """One GEMM-unit of one head: 2*d flop per kept pair."""
+    return 2 * b["d"] * causal_pairs(b["n"])
 
 
 def memory_report(bufs, base_alloc, peak_alloc, free_before, free_after_alloc, free_after_steps):
@@ -646,11 +684,12 @@ def extra_workload(name, args, dev):
     peak = torch.cuda.max_memory_allocated() - base_alloc
     memory = memory_report(bufs, base_alloc, peak, free_before, free_after_alloc, free_after_steps)
     flops = sum(6 * units(b) for b in bufs)
-    ms_maps = time_fused_maps(bufs, w.scale, args.extra_steps, 1)
+    ms_maps = time_fused_maps(bufs, w.scale, args.extra_steps, 2)
     out = {"workload": name, "B": w.B, "n": w.n, "d": w.d, "heads": w.heads, "steps": args.extra_steps,
            "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
            "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-           "kernels_avg_ms": {k: round(float(np.mean(v)), 4) for k, v in per_kernel.items()},
+           "kernels_avg_ms": {k: round(v, 4) for k, v in kernel_ms(per_kernel).items()},
+           "heads_per_group": {b["name"]: b["groups"][0]["heads"] for b in bufs},
            "phase2_mode": mode, f"ms_per_step_{other}_phase2": round(ms_other, 4),
            "fused_maps_ms_per_step": round(ms_maps, 4),
            "losses": {b["name"]: float(b["loss"].cpu()) for b in bufs},
@@ -708,7 +747,7 @@ def main():
     # other mode larard_kl_bwd offers; AUTO takes the split one).
     ms_fused, per_fused, _, _ = run_steps(bufs, scale, args.steps, 1, mode="fused")
     phase2_fused = {"ms_per_step": round(ms_fused, 4),
-                    "kernels_avg_ms": {k: round(float(np.mean(v)), 4) for k, v in per_fused.items()},
+                    "kernels_avg_ms": {k: round(v, 4) for k, v in kernel_ms(per_fused).items()},
                     "what": "phase 2 as one launch per map (LARARD_DX_FUSED): each row block's row and column "
                             "terms in one sweep, dX_s stored once"}
     peak_alloc = torch.cuda.max_memory_allocated() - base_alloc
@@ -738,22 +777,28 @@ def main():
     # contraction (GEMM-unit) = 2*d*P flops.  Phase 1: 2 units; phase 2: 4
     # (the logit recompute of both maps, the row term and the column term),
     # executed as 6 because phase 2 forms every logit tile twice.
+    # Every launch's algorithmic and executed flops follow from its head count
+    # (a head group of one map; the maps of one workload share n and d).
+    uph = units_per_head(bufs[0])
     kern = {}
     for kind in KINDS["split"]:
-        t = float(np.mean(per_kernel[kind]))
-        fl = np.mean([ALG[kind] * units(b) for b in bufs])
-        fe = np.mean([EXE[kind] * units(b) for b in bufs])
-        kern[kind] = {"avg_ms": t, "share": float(np.sum(per_kernel[kind]) / total_ms),
-                      "alg_tflops": fl / (t * 1e-3) / 1e12 if fl else 0.0,
-                      "executed_tflops": fe / (t * 1e-3) / 1e12 if fe else 0.0}
+        ms_l = np.array([t for t, _ in per_kernel[kind]])
+        heads_l = np.array([hh for _, hh in per_kernel[kind]], dtype=np.float64)
+        fl, fe = ALG[kind] * uph * heads_l, EXE[kind] * uph * heads_l
+        kern[kind] = {"avg_ms": float(ms_l.mean()), "launches_per_step": len(ms_l) // args.steps,
+                      "heads_per_launch": float(heads_l.mean()),
+                      "share": float(ms_l.sum() / total_ms),
+                      "alg_flops_per_launch": float(fl.mean()),
+                      "alg_tflops": float(fl.sum() / (ms_l.sum() * 1e-3) / 1e12),
+                      "executed_tflops": float(fe.sum() / (ms_l.sum() * 1e-3) / 1e12)}
 
     # Roofline of every sweep kernel; `roofline` is the one with the largest
     # share of the step's time.  Counter-derived figures (HBM traffic, MFMA and
     # VALU busy fractions, executed flops) come from the committed rocprofv3
     # summary when it was taken on a library built from the same sources.
     def roof(kind):
-        fl = float(np.mean([ALG[kind] * units(b) for b in bufs]))
-        ach = fl / (kern[kind]["avg_ms"] * 1e-3) / 1e12
+        fl = kern[kind]["alg_flops_per_launch"]
+        ach = kern[kind]["alg_tflops"]
         ctr = recorded_counters(kind, w.name)
         return {"kernel": kind, "bound": "mfma", "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),

@@ -107,6 +107,22 @@ typedef enum { LARARD_DX_AUTO = 0, LARARD_DX_SPLIT = 1, LARARD_DX_ATOMIC = 2, LA
  * Returns 0 for invalid sizes. */
 size_t larard_workspace_bytes(larard_dtype dtype, int64_t B, int64_t H, int64_t n);
 
+/* Heads per group of the whole-path calls with a gradient (larard_loss,
+ * larard_loss_noalloc, larard_xy_loss, and larard_multi_loss when its maps
+ * run apart): they run phase 1 and phase 2 for heads [h0, h0+g) of the
+ * flattened B*H heads before the next group, so that the group's
+ * projections are still in the GPU's 256 MB last-level cache when phase 2
+ * re-reads them.  g is the largest head count whose bf16 projections
+ * (X_t, X_s, and Y_t, Y_s when cross != 0) fit 256 MiB, raised if needed to
+ * ceil(1024 / ceil(n/256)) heads so that each sweep still has 1024
+ * workgroups, and capped at B*H.  fp32 inputs run as one group.  A caller
+ * of larard_lse_fwd / larard_kl_bwd can slice its heads the same way.
+ * Measured on MI355X (ms per step, one group -> groups of 8 or 16 heads):
+ * n = 32K 105.3 -> 101.7; at n = 16K (32 heads, one group) grouping gained
+ * nothing.  Results are the same bits either way.  Returns 0 for invalid
+ * sizes. */
+int64_t larard_loss_head_group(larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d, int cross);
+
 /* Phase 1 (notes page, "Key designs" item 3; summary page, "Method"):
  * streams key tiles and writes
  *   lse_t[b,h,i] = log sum_{j kept} exp(scale * <x_t,i , x_t,j>)

@@ -2,6 +2,7 @@
 // workspace carving and kernel dispatch.  No device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -130,6 +131,59 @@ larard_status run_kl_bwd(lmr::SweepArgs a, float loss_scale, int dx_mode, hipStr
   return LARARD_OK;
 }
 
+// Whole-path calls (loss with gradient) run phase 1 and phase 2 head group by
+// head group (larard.h, larard_loss_head_group): a group's projections are
+// then still in the last-level cache when its phase-2 sweeps re-read them.
+// Measured on MI355X, ms per step, all heads at once -> grouped: n = 32K
+// 105.3 -> 101.7 (split), 107.3 -> 101.8 (fused); at n = 16K one group of
+// 32 heads (split 25.7) and two of 16 (25.9) are equal within noise, and
+// two groups would cost phase 1 its 12-wave shape, so 16K stays one group.
+// Every head's arithmetic is its own, so the results are the same bits
+// either way.
+constexpr int64_t kGroupBytes = int64_t(256) << 20;
+constexpr int64_t kGroupGrid = 1024;
+
+int64_t group_of(bool fp32, bool cross, int64_t bh, int64_t n, int64_t d) {
+  if (fp32) return bh;
+  const int64_t per_head = (cross ? 4 : 2) * n * d * 2;
+  const int64_t rows_blk = (n + 255) / 256;
+  int64_t g = per_head > 0 ? kGroupBytes / per_head : bh;
+  if (rows_blk > 0) g = std::max(g, (kGroupGrid + rows_blk - 1) / rows_blk);
+  return std::max<int64_t>(1, std::min(g, bh));
+}
+
+int64_t head_group(const lmr::SweepArgs& a) { return group_of(a.fp32 != 0, a.cross != 0, a.bh, a.n, a.d); }
+
+// The argument set of heads h0 .. h0+cnt-1 of a (bf16 inputs, fp64 statistics).
+lmr::SweepArgs head_slice(const lmr::SweepArgs& a, int64_t h0, int64_t cnt) {
+  lmr::SweepArgs g = a;
+  const int64_t xo = h0 * a.n * a.d * (a.fp32 ? 4 : 2), ro = h0 * a.n, go = h0 * a.n * a.d;
+  g.xt = static_cast<const char*>(a.xt) + xo;
+  g.xs = static_cast<const char*>(a.xs) + xo;
+  g.yt = static_cast<const char*>(a.yt) + xo;
+  g.ys = static_cast<const char*>(a.ys) + xo;
+  g.lse_t = static_cast<double*>(a.lse_t) + ro;
+  g.lse_s = static_cast<double*>(a.lse_s) + ro;
+  g.row_kl = a.row_kl + ro;
+  g.dx = a.dx != nullptr ? a.dx + go : nullptr;
+  g.dy = a.dy != nullptr ? a.dy + go : nullptr;
+  g.bh = cnt;
+  return g;
+}
+
+// Phase 1 and phase 2 of a whole-path call with a gradient, group by group.
+larard_status run_grouped(const lmr::SweepArgs& a, float loss_scale, int dx_mode, hipStream_t st) {
+  const int64_t g = head_group(a);
+  for (int64_t h0 = 0; h0 < a.bh; h0 += g) {
+    const lmr::SweepArgs part = head_slice(a, h0, std::min(g, a.bh - h0));
+    const hipError_t e = lmr::launch_lse_fwd(part, st);
+    if (e != hipSuccess) return hip_fail(e, "lse_fwd launch");
+    const larard_status s = run_kl_bwd(part, loss_scale, dx_mode, st);
+    if (s != LARARD_OK) return s;
+  }
+  return LARARD_OK;
+}
+
 // Validation shared by the phase-2 entry points; fills *out on success.
 larard_status check_phase2(const void* x_t, const void* x_s, larard_dtype dtype, int64_t B, int64_t H, int64_t n,
                            int64_t d, float scale, int causal, const void* lse_t, const void* lse_s,
@@ -189,10 +243,8 @@ larard_status run_loss(const void* x_t, const void* x_s, larard_dtype dtype, int
     e = lmr::launch_kl_fwd(a, st);
     if (e != hipSuccess) return hip_fail(e, "kl_fwd launch");
   } else {
-    e = lmr::launch_lse_fwd(a, st);
-    if (e != hipSuccess) return hip_fail(e, "lse_fwd launch");
     a.dx = dx_s;
-    if ((s = run_kl_bwd(a, loss_scale, dx_mode, st)) != LARARD_OK) return s;
+    if ((s = run_grouped(a, loss_scale, dx_mode, st)) != LARARD_OK) return s;
   }
   e = lmr::launch_reduce(a.row_kl, a.bh, a.n, loss_scale, partials, loss, st);
   if (e != hipSuccess) return hip_fail(e, "loss reduction launch");
@@ -236,6 +288,12 @@ size_t larard_workspace_bytes(larard_dtype dtype, int64_t B, int64_t H, int64_t 
   size_t off[4];
   if (larard_workspace_layout(dtype, B, H, n, off) != LARARD_OK) return 0;
   return off[3] + align256((size_t)(B * H) * sizeof(double));
+}
+
+int64_t larard_loss_head_group(larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d, int cross) {
+  if (B < 1 || H < 1 || n < 0 || n > kMaxN || B > kMaxGrid / H || (d != 64 && d != 128)) return 0;
+  if (dtype != LARARD_BF16 && dtype != LARARD_FP32) return 0;
+  return group_of(dtype == LARARD_FP32, cross != 0, B * H, n, d);
 }
 
 larard_status larard_workspace_layout(larard_dtype dtype, int64_t B, int64_t H, int64_t n, size_t off[4]) {
@@ -465,11 +523,9 @@ larard_status larard_xy_loss(const void* x_t, const void* x_s, const void* y_t, 
     e = lmr::launch_kl_fwd(a, st);
     if (e != hipSuccess) return hip_fail(e, "xy_kl_fwd launch");
   } else {
-    e = lmr::launch_lse_fwd(a, st);
-    if (e != hipSuccess) return hip_fail(e, "xy_lse_fwd launch");
     a.dx = dx_s;
     a.dy = dy_s;
-    if ((s = run_kl_bwd(a, loss_scale, LARARD_DX_SPLIT, st)) != LARARD_OK) return s;
+    if ((s = run_grouped(a, loss_scale, LARARD_DX_SPLIT, st)) != LARARD_OK) return s;
   }
   e = lmr::launch_reduce(a.row_kl, a.bh, a.n, loss_scale, partials, loss, st);
   if (e != hipSuccess) return hip_fail(e, "loss reduction launch");
@@ -592,12 +648,11 @@ larard_status larard_multi_loss(const larard_map* maps, int n_maps, larard_dtype
   } else if (maps_run_apart(maps, n_maps, B, n, set.map[0])) {
     // Every map fills the GPU on its own: its three sweeps run back to back,
     // while its projections are still in the last-level cache.
-    for (int m = 0; m < n_maps && e == hipSuccess; ++m) {
-      e = lmr::launch_lse_fwd(set.map[m], st);
-      if (e == hipSuccess) e = lmr::launch_kl_row(set.map[m], st);
-      if (e == hipSuccess) e = lmr::launch_kl_col(set.map[m], st);
+    for (int m = 0; m < n_maps; ++m) {
+      // grad_scale already carries the map's weight; run_kl_bwd sets it
+      // from loss_scale, so pass the weighted scale.
+      if ((s = run_grouped(set.map[m], loss_scale * maps[m].weight, LARARD_DX_SPLIT, st)) != LARARD_OK) return s;
     }
-    if (e != hipSuccess) return hip_fail(e, "per-map sweep launch");
   } else {
     if ((e = lmr::launch_lse_fwd_multi(set, st)) != hipSuccess) return hip_fail(e, "multi-map lse_fwd launch");
     if (use_fused(set.map[0], LARARD_DX_AUTO)) {

@@ -281,3 +281,23 @@ def test_noalloc_validation_before_any_device_access(lib):
     assert call(mode=2) == 2
     assert call(d=96) == 2
     assert call(xt=None) == 1
+
+
+def test_loss_head_group_sizes(lib):
+    """Heads per group of the whole-path calls: 256 MiB of bf16 projections per
+    group, at least 1024 sweep workgroups, at most B*H; fp32 runs as one group."""
+    hg = lib.larard_loss_head_group
+    hg.restype = ctypes.c_int64
+    hg.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+    assert hg(0, 1, 32, 16384, 128, 0) == 32          # 8 MiB per head: the whole map
+    assert hg(0, 1, 32, 32768, 128, 0) == 16          # 16 MiB per head
+    assert hg(0, 1, 32, 4096, 128, 0) == 32
+    assert hg(0, 2, 32, 8192, 128, 0) == 64           # 4 MiB per head: all 64 heads
+    assert hg(0, 1, 32, 32768, 128, 1) == 8           # cross: 32 MiB per head; 128 row blocks x 8 = 1024
+    assert hg(0, 1, 32, 16384, 128, 1) == 16          # cross: 16 MiB per head
+    assert hg(0, 1, 64, 65536, 128, 0) == 8           # 32 MiB per head
+    assert hg(0, 1, 16, 131072, 128, 0) == 4          # 64 MiB per head: 4 heads x 512 row blocks = 2048
+    assert hg(0, 1, 16, 262144, 128, 0) == 2          # 128 MiB per head: 2 heads x 1024 row blocks
+    assert hg(1, 1, 32, 32768, 128, 0) == 32          # fp32 precision kernels: one group
+    assert hg(0, 1, 32, 0, 128, 0) == 32
+    assert hg(0, 0, 32, 16384, 128, 0) == 0 and hg(0, 1, 32, 16384, 96, 0) == 0 and hg(7, 1, 32, 16, 64, 0) == 0

@@ -394,3 +394,28 @@ def test_auto_mode_choice(gpu_lib, n, expect):
     torch.cuda.synchronize()
     assert torch.equal(d_auto, d_want)
     assert not torch.equal(d_auto, d_other)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_head_groups_match_one_launch(gpu_lib, mode):
+    """larard_loss runs phase 1 and phase 2 head group by head group (here 64
+    heads at n = 8448, d = 128: groups of 62 and 2, larard_loss_head_group);
+    its loss and gradient equal those of the phase entry points launched once
+    over all heads, bit for bit."""
+    import torch
+    B, H, n, d = 1, 64, 8448, 128
+    assert gpu_lib.loss_head_group(B, H, n, d) == 62
+    xt, xs = random_pair(B, H, n, d, 0.3, seed=21)
+    a, b = to_device(xt, "bf16"), to_device(xs, "bf16")
+    s = 1.0 / np.sqrt(d)
+    loss_g, dx_g = gpu_lib.loss(a, b, s, True, 0.5, dx_mode=mode)
+    lse_t = torch.empty((B, H, n), dtype=torch.float64, device="cuda")
+    lse_s = torch.empty_like(lse_t)
+    gpu_lib.lse_fwd(a, b, s, True, lse_t, lse_s)
+    row_kl, dx1 = gpu_lib.kl_bwd(a, b, lse_t, lse_s, s, True, 0.5, dx_mode=mode)
+    partials = torch.empty((B * H,), dtype=torch.float64, device="cuda")
+    loss1 = torch.empty((), dtype=torch.float32, device="cuda")
+    gpu_lib.reduce_loss(row_kl, partials, loss1, 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(dx_g, dx1)
+    assert float(loss_g.cpu()) == float(loss1.cpu())
