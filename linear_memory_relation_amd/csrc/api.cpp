@@ -140,7 +140,10 @@ larard_status run_kl_bwd(lmr::SweepArgs a, float loss_scale, int dx_mode, hipStr
 // two groups would cost phase 1 its 12-wave shape, so 16K stays one group.
 // Every head's arithmetic is its own, so the results are the same bits
 // either way.
-constexpr int64_t kGroupBytes = int64_t(256) << 20;
+#ifndef LMR_GROUP_MIB
+#define LMR_GROUP_MIB 256
+#endif
+constexpr int64_t kGroupBytes = int64_t(LMR_GROUP_MIB) << 20;
 constexpr int64_t kGroupGrid = 1024;
 
 int64_t group_of(bool fp32, bool cross, int64_t bh, int64_t n, int64_t d) {
