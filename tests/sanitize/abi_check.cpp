@@ -38,6 +38,12 @@ int main() {
   if (larard_workspace_bytes(bf, big, big, 1) != 0) { std::printf("FAIL huge B*H accepted\n"); ++g_fail; }
   if (larard_workspace_bytes(bf, 1, 1, (int64_t(1) << 24) + 1) != 0) { std::printf("FAIL huge n accepted\n"); ++g_fail; }
   if (larard_workspace_bytes(f32, 0, 1, 4) != 0) { std::printf("FAIL B=0 accepted\n"); ++g_fail; }
+  // head groups of the whole-path calls (overflow-prone products of sizes)
+  if (larard_loss_head_group(bf, 1, 32, 16384, 128, 0) != 32) { std::printf("FAIL head group 16K\n"); ++g_fail; }
+  if (larard_loss_head_group(bf, 1, 32, 32768, 128, 1) != 8) { std::printf("FAIL head group cross\n"); ++g_fail; }
+  if (larard_loss_head_group(bf, big, big, 64, 128, 0) != 0) { std::printf("FAIL huge head group accepted\n"); ++g_fail; }
+  if (larard_loss_head_group(bf, 1, 1, int64_t(1) << 24, 128, 1) != 1) { std::printf("FAIL head group max n\n"); ++g_fail; }
+  if (larard_loss_head_group(bf, 1, 4, -1, 128, 0) != 0) { std::printf("FAIL negative n accepted\n"); ++g_fail; }
   size_t off[4];
   expect("layout null", larard_workspace_layout(bf, 1, 1, 4, nullptr), LARARD_E_INVALID);
   expect("layout", larard_workspace_layout(bf, 2, 8, 8192, off), LARARD_OK);
