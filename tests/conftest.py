@@ -22,3 +22,24 @@ def gpu_lib():
     import linear_memory_relation_amd as lmr
     lmr.load()      # raises if the built library is missing
     return lmr
+
+
+# Parity figures that the GPU tests print (loss_rel, max-rel errors) are
+# repeated in a section of the terminal summary, so that a quiet run's log
+# still carries them.
+_PARITY_KEYS = ("loss_rel", "maxrel", "max-rel", "lse_err", "kl_err")
+_parity_lines = []
+
+
+def pytest_runtest_logreport(report):
+    if report.when == "call" and report.passed and report.capstdout:
+        for line in report.capstdout.splitlines():
+            if any(k in line for k in _PARITY_KEYS):
+                _parity_lines.append(f"{report.nodeid.split('::')[-1]}: {line.strip()}")
+
+
+def pytest_terminal_summary(terminalreporter):
+    if _parity_lines:
+        terminalreporter.section("parity figures printed by the passing tests")
+        for line in _parity_lines:
+            terminalreporter.write_line(line)
