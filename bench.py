@@ -51,6 +51,11 @@ def parse():
                    help="comma-separated workloads timed after the headline one (same step, fewer steps); "
                         "empty to skip")
     p.add_argument("--extra-steps", type=int, default=5)
+    p.add_argument("--proj-only", action="store_true",
+                   help="time only the projection backward of every map of --workload (model width = the "
+                        "first map's H*d) after one step has produced dX_s, and print one JSON line")
+    p.add_argument("--trace-table", metavar="TRACE_DIR",
+                   help="print a markdown table of every kernel of a rocprofv3 --kernel-trace run and exit")
     p.add_argument("--core-only", action="store_true",
                    help="time only the step (and its one-call check): skip the forward-only, fused-map, "
                         "projection and cross-relation sections, whose launches share kernel symbols with "
@@ -343,6 +348,57 @@ def recorded_counters(kind: str, workload: str):
     return vals
 
 
+def time_proj(b, w, dev, dm, steps, warmup):
+    """ms and TFLOP/s of larard_proj_bwd for map b: dW [dm, H*d] = h^T R^T(dX_s) with synthetic bf16
+    hidden states h [B, n, dm], the map's dX_s as the last step left it, and the student rotation of
+    the workload (none for V)."""
+    import torch
+    import linear_memory_relation_amd as lmr
+    hd = b["H"] * b["d"]
+    if dm % 128 or hd % 128:
+        return None
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    hst = torch.randn((b["B"], b["n"], dm), generator=g, device=dev).to(torch.bfloat16)
+    rc = rs = None
+    if b["name"] != "V":
+        pos = torch.arange(b["n"], dtype=torch.float64) / (w.factor if w.kind == "pi" else 1.0)
+        inv = (w.base * (w.factor ** (b["d"] / (b["d"] - 2)) if w.kind == "ntk" else w.base)) ** (
+            -2.0 * torch.arange(b["d"] // 2, dtype=torch.float64) / b["d"])
+        ang = torch.outer(pos, inv)
+        rc, rs = torch.cos(ang).float().to(dev), torch.sin(ang).float().to(dev)
+    wsp = torch.empty(max(256, int(lmr.load().larard_proj_bwd_workspace_bytes(b["B"], b["n"], dm, b["H"], b["d"]))),
+                      dtype=torch.uint8, device=dev)
+    dW = torch.empty((dm, hd), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        lmr.proj_bwd(hst, b["dx"], rc, rs, workspace=wsp, out=dW)
+    torch.cuda.synchronize()
+    s6, e6 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s6.record()
+    for _ in range(steps):
+        lmr.proj_bwd(hst, b["dx"], rc, rs, workspace=wsp, out=dW)
+    e6.record()
+    torch.cuda.synchronize()
+    ms_p = s6.elapsed_time(e6) / steps
+    pflops = 2.0 * dm * hd * b["B"] * b["n"]
+    del hst, wsp, dW
+    return {"ms": round(ms_p, 4), "tflops": round(pflops / (ms_p * 1e-3) / 1e12, 3),
+            "pct_bf16_peak": round(100 * pflops / (ms_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "what": f"larard_proj_bwd for map {b['name']}: dW [{dm}x{hd}] = h^T R^T(dX_s), "
+                    f"K = B*n = {b['B'] * b['n']}; synthetic bf16 h; flops 2*dm*H*d*B*n"}
+
+
+def trace_table(trace_dir: str) -> str:
+    """Markdown table of every kernel of a rocprofv3 --kernel-trace run."""
+    rows = _trace_stats(trace_dir)
+    total = sum(r[5] for r in rows)
+    out = ["| kernel | calls | avg ms | min ms | max ms | share of GPU time |", "|---|---|---|---|---|---|"]
+    for name, calls, avg, mn, mx, tot in rows:
+        out.append(f"| `{name[:100]}` | {calls} | {avg / 1e6:.4f} | {mn / 1e6:.4f} | {mx / 1e6:.4f} | "
+                   f"{100 * tot / total:.2f}% |")
+    return "\n".join(out) + "\n"
+
+
 def extra_sections(args, bufs, w, scale, dev, units, step_flops):
     """Timings beside the step: forward-only loss, all maps fused in one launch
     per phase, the projection backward and the query/key cross relation."""
@@ -398,37 +454,7 @@ def extra_sections(args, bufs, w, scale, dev, units, step_flops):
 
     # Projection backward of the first map: dW = h^T R^T(dX_s) with synthetic
     # bf16 hidden states of model width H*d and the student rotation (PI).
-    proj = None
-    bq0 = bufs[0]
-    dm = bq0["H"] * bq0["d"]
-    if dm % 128 == 0:
-        g = torch.Generator(device=dev)
-        g.manual_seed(1234)
-        hst = torch.randn((bq0["B"], bq0["n"], dm), generator=g, device=dev).to(torch.bfloat16)
-        pos = torch.arange(bq0["n"], dtype=torch.float64) / (w.factor if w.kind == "pi" else 1.0)
-        inv = (w.base * (w.factor ** (bq0["d"] / (bq0["d"] - 2)) if w.kind == "ntk" else w.base)) ** (
-            -2.0 * torch.arange(bq0["d"] // 2, dtype=torch.float64) / bq0["d"])
-        ang = torch.outer(pos, inv)
-        rc, rs = torch.cos(ang).float().to(dev), torch.sin(ang).float().to(dev)
-        wsp = torch.empty(int(lmr.load().larard_proj_bwd_workspace_bytes(bq0["B"], bq0["n"], dm, bq0["H"], bq0["d"])),
-                          dtype=torch.uint8, device=dev)
-        dW = torch.empty((dm, dm), dtype=torch.float32, device=dev)
-        for _ in range(args.warmup):
-            lmr.proj_bwd(hst, bq0["dx"], rc, rs, workspace=wsp, out=dW)
-        torch.cuda.synchronize()
-        s6, e6 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s6.record()
-        for _ in range(args.steps):
-            lmr.proj_bwd(hst, bq0["dx"], rc, rs, workspace=wsp, out=dW)
-        e6.record()
-        torch.cuda.synchronize()
-        ms_p = s6.elapsed_time(e6) / args.steps
-        pflops = 2.0 * dm * dm * bq0["B"] * bq0["n"]
-        proj = {"ms": round(ms_p, 4), "tflops": round(pflops / (ms_p * 1e-3) / 1e12, 3),
-                "pct_bf16_peak": round(100 * pflops / (ms_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                "what": f"larard_proj_bwd for map {bq0['name']}: dW [{dm}x{dm}] = h^T R^T(dX_s), "
-                        f"K = B*n = {bq0['B'] * bq0['n']}; synthetic bf16 h; flops 2*dm*H*d*B*n"}
-        del hst, wsp, dW
+    proj = time_proj(bufs[0], w, dev, bufs[0]["H"] * bufs[0]["d"], args.steps, args.warmup)
 
     # General relation X != Y on the same data: the query/key map (X = Q,
     # Y = K), fwd+bwd through one larard_xy_loss call (dX_s and dY_s).
@@ -705,6 +731,9 @@ def main():
     if args.summarize:
         sys.stdout.write(summarize(args.summarize[0], args.summarize[1], args.pmc_dir, args.trace_cmd))
         return
+    if args.trace_table:
+        sys.stdout.write(trace_table(args.trace_table))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this kernel shards by heads "
               f"with no exchange but a scalar loss sum; this benchmark measures a single GPU.",
@@ -722,6 +751,14 @@ def main():
     dev = torch.device("cuda:0")
     w = si.WORKLOADS[args.workload]
     scale = w.scale
+    if args.proj_only:
+        maps, bufs = make_buffers(w, dev)
+        run_steps(bufs, scale, 1, 1, events=False)          # dX_s of every map
+        dm = bufs[0]["H"] * bufs[0]["d"]
+        print(json.dumps({"workload": w.name, "proj_bwd": {b["name"]: time_proj(b, w, dev, dm, args.steps,
+                                                                                 args.warmup) for b in bufs}}),
+              flush=True)
+        return
 
     torch.cuda.synchronize()
     free_before = torch.cuda.mem_get_info()[0]
