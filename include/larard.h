@@ -193,8 +193,9 @@ larard_status larard_reduce_loss(const float* row_kl, int64_t B, int64_t H, int6
 /* Whole path for one relation map: phase 1, phase 2 and a deterministic
  * fp64 reduction.  Writes
  *   *loss = loss_scale * sum_{b,h} (1/n) sum_i KL_i        (device fp32 scalar)
- * and dx_s as in larard_kl_bwd.  dx_s == NULL computes the loss only, with
- * larard_kl_fwd's single sweep instead of phase 1 + phase 2.  The workspace (device,
+ * and dx_s as in larard_kl_bwd (same bits).  Phase 1 and phase 2 run head
+ * group by head group (larard_loss_head_group).  dx_s == NULL computes the
+ * loss only, with larard_kl_fwd's single sweep instead of phase 1 + phase 2.  The workspace (device,
  * 256-byte aligned, >= larard_workspace_bytes(dtype,B,H,n)) holds LSE_t, LSE_s,
  * row_kl and partial sums; after return-and-sync it contains them in that
  * order (see larard_workspace_layout).  n == 0 writes *loss = 0. */
