@@ -254,11 +254,12 @@ def summarize(trace_dir: str, copy_mib: str, pmc_dirs, cmds: str) -> str:
         import linear_memory_relation_amd as lmr
         from synth_inputs import WORKLOADS
         w = WORKLOADS["llama2_16k"]
-        hpl = lmr.loss_head_group(w.B, 32, w.n, w.d)   # heads per launch: one head group of one map
-        unit = hpl * 2 * w.d * causal_pairs(w.n)      # one GEMM-unit over the heads of one launch
+        hp1 = lmr.loss_head_group(w.B, 32, w.n, w.d)    # heads per phase-1 launch (a head group of a map)
+        hp2 = lmr.loss_sweep_group(w.B, 32, w.n, w.d)   # heads per phase-2 launch (a sub-group)
+        unit = {k: (hp1 if k == "lse_fwd" else hp2) * 2 * w.d * causal_pairs(w.n) for k in ALG_UNITS}
         lines += ["", "## MFMA and VALU utilisation (rocprofv3 --pmc, one dispatch at a time)", ""]
-        lines += [f"Per sweep kernel, mean over its dispatches (one per head group of {hpl} heads of a map; "
-                  "the step runs phase 1 and phase 2 group by group):",
+        lines += [f"Per sweep kernel, mean over its dispatches (phase 1: one per head group of {hp1} heads of a "
+                  f"map; phase 2: one per sub-group of {hp2} heads):",
                   "- `clock` = GRBM_GUI_ACTIVE per XCD / kernel-trace average duration;",
                   "- `MFMA busy` = sum of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs) "
                   "(AMD's MfmaUtil expression);",
@@ -282,7 +283,7 @@ def summarize(trace_dir: str, copy_mib: str, pmc_dirs, cmds: str) -> str:
             vb = valu.get(kind, float("nan")) / CU_NUM / g
             ef = mops.get(kind, float("nan")) * 512
             ei = nmfma.get(kind, float("nan")) * FLOPS_PER_MFMA
-            af = ALG_UNITS[kind] * unit
+            af = ALG_UNITS[kind] * unit[kind]
             co = coex.get(kind, float("nan")) / (g * SIMD_NUM)
             lines.append(f"| {kind} | {clk:.3f} | {mb:.3f} | {vb:.3f} | {co:.3f} | {ef:.4e} | {ei:.4e} | {af:.4e} | "
                          f"{ef / af:.3f} |")
@@ -514,20 +515,26 @@ def make_buffers(w, dev):
 
 
 def head_groups(b):
-    """Views of one map's tensors per head group, as larard_loss schedules them: phase 1 and
-    phase 2 run for heads [h0, h0+g) of the flattened B*H heads before the next group
-    (larard_loss_head_group), so that the group's projections stay in the last-level cache."""
+    """Views of one map's tensors as larard_loss schedules its heads: phase 1 and phase 2 run for
+    heads [h0, h0+g) of the flattened B*H heads before the next group (larard_loss_head_group),
+    and within a group phase 2 runs per sub-group (larard_loss_sweep_group), so that the heads'
+    projections stay in the last-level cache between the sweeps that read them."""
     import linear_memory_relation_amd as lmr
     bh, n, d = b["B"] * b["H"], b["n"], b["d"]
-    g = lmr.loss_head_group(b["B"], b["H"], n, d)
-    out = []
-    for h0 in range(0, bh, g):
-        c = min(g, bh - h0)
+    g1 = lmr.loss_head_group(b["B"], b["H"], n, d)
+    g2 = lmr.loss_sweep_group(b["B"], b["H"], n, d)
 
+    def views(h0, c):
         def sl(t, tail):
             return t.reshape(1, bh, *tail)[:, h0:h0 + c]
-        out.append(dict(heads=c, xt=sl(b["xt"], (n, d)), xs=sl(b["xs"], (n, d)), lse_t=sl(b["lse_t"], (n,)),
-                        lse_s=sl(b["lse_s"], (n,)), row_kl=sl(b["row_kl"], (n,)), dx=sl(b["dx"], (n, d))))
+        return dict(heads=c, xt=sl(b["xt"], (n, d)), xs=sl(b["xs"], (n, d)), lse_t=sl(b["lse_t"], (n,)),
+                    lse_s=sl(b["lse_s"], (n,)), row_kl=sl(b["row_kl"], (n,)), dx=sl(b["dx"], (n, d)))
+    out = []
+    for h0 in range(0, bh, g1):
+        c = min(g1, bh - h0)
+        grp = views(h0, c)
+        grp["sub"] = [views(k0, min(g2, h0 + c - k0)) for k0 in range(h0, h0 + c, g2)]
+        out.append(grp)
     return out
 
 
@@ -549,11 +556,13 @@ def run_steps(bufs, scale, steps, warmup, events=True, mode="split"):
     seconds of the timed region); per-kernel entries are (ms, heads of the launch)."""
     import torch
     import linear_memory_relation_amd as lmr
-    phases = KINDS[mode][:-1]
+    sweeps = KINDS[mode][1:-1]
     plan = []                      # kinds of one step's launches, in order, with their head counts
     for b in bufs:
         for grp in b["groups"]:
-            plan += [(k, grp["heads"]) for k in phases]
+            plan.append(("lse_fwd", grp["heads"]))
+            for sg in grp["sub"]:
+                plan += [(k, sg["heads"]) for k in sweeps]
         plan.append(("reduce", b["B"] * b["H"]))
 
     def step(ev=None):
@@ -565,17 +574,17 @@ def run_steps(bufs, scale, steps, warmup, events=True, mode="split"):
         mark()
         for b in bufs:
             for grp in b["groups"]:
-                a = (grp["xt"], grp["xs"])
-                lmr.lse_fwd(*a, scale, True, grp["lse_t"], grp["lse_s"])
+                lmr.lse_fwd(grp["xt"], grp["xs"], scale, True, grp["lse_t"], grp["lse_s"])
                 mark()
-                if mode == "fused":
-                    lmr.kl_bwd(*a, grp["lse_t"], grp["lse_s"], scale, True, 1.0, dx_mode=lmr.DX_FUSED,
-                               row_kl=grp["row_kl"], dx=grp["dx"])
-                else:
-                    lmr.kl_bwd_rows(*a, grp["lse_t"], grp["lse_s"], grp["row_kl"], grp["dx"], scale, True, 1.0)
+                for sg in grp["sub"]:
+                    a = (sg["xt"], sg["xs"], sg["lse_t"], sg["lse_s"])
+                    if mode == "fused":
+                        lmr.kl_bwd(*a, scale, True, 1.0, dx_mode=lmr.DX_FUSED, row_kl=sg["row_kl"], dx=sg["dx"])
+                    else:
+                        lmr.kl_bwd_rows(*a, sg["row_kl"], sg["dx"], scale, True, 1.0)
+                        mark()
+                        lmr.kl_bwd_cols(*a, sg["dx"], scale, True, 1.0)
                     mark()
-                    lmr.kl_bwd_cols(*a, grp["lse_t"], grp["lse_s"], grp["dx"], scale, True, 1.0)
-                mark()
             lmr.reduce_loss(b["row_kl"], b["partials"], b["loss"], 1.0)
             mark()
 
@@ -715,7 +724,8 @@ def extra_workload(name, args, dev):
            "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
            "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
            "kernels_avg_ms": {k: round(v, 4) for k, v in kernel_ms(per_kernel).items()},
-           "heads_per_group": {b["name"]: b["groups"][0]["heads"] for b in bufs},
+           "heads_per_group": {b["name"]: [b["groups"][0]["heads"], b["groups"][0]["sub"][0]["heads"]]
+                               for b in bufs},
            "phase2_mode": mode, f"ms_per_step_{other}_phase2": round(ms_other, 4),
            "fused_maps_ms_per_step": round(ms_maps, 4),
            "losses": {b["name"]: float(b["loss"].cpu()) for b in bufs},

@@ -123,6 +123,15 @@ size_t larard_workspace_bytes(larard_dtype dtype, int64_t B, int64_t H, int64_t 
  * sizes. */
 int64_t larard_loss_head_group(larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d, int cross);
 
+/* Heads per phase-2 sub-group of the same calls: within each head group,
+ * phase 2 (the row and column sweeps, or the fused sweep, which read a
+ * head's projections twice) runs for sub-groups of at most this many heads,
+ * the same rule with a 128 MiB budget (still at least 1024 workgroups per
+ * sweep).  Measured on MI355X (ms per step, phase 2 per group -> per
+ * sub-group): n = 16K 25.7 -> 25.4 (split), GQA 8K 6.93 -> 6.68 (fused).
+ * Returns 0 for invalid sizes. */
+int64_t larard_loss_sweep_group(larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d, int cross);
+
 /* Phase 1 (notes page, "Key designs" item 3; summary page, "Method"):
  * streams key tiles and writes
  *   lse_t[b,h,i] = log sum_{j kept} exp(scale * <x_t,i , x_t,j>)
@@ -194,7 +203,7 @@ larard_status larard_reduce_loss(const float* row_kl, int64_t B, int64_t H, int6
  * fp64 reduction.  Writes
  *   *loss = loss_scale * sum_{b,h} (1/n) sum_i KL_i        (device fp32 scalar)
  * and dx_s as in larard_kl_bwd (same bits).  Phase 1 and phase 2 run head
- * group by head group (larard_loss_head_group).  dx_s == NULL computes the
+ * group by head group (larard_loss_head_group, larard_loss_sweep_group).  dx_s == NULL computes the
  * loss only, with larard_kl_fwd's single sweep instead of phase 1 + phase 2.  The workspace (device,
  * 256-byte aligned, >= larard_workspace_bytes(dtype,B,H,n)) holds LSE_t, LSE_s,
  * row_kl and partial sums; after return-and-sync it contains them in that
@@ -282,12 +291,12 @@ larard_status larard_xy_loss(const void* x_t, const void* x_s, const void* y_t, 
  * runs once over the heads of all maps, saving the launch gaps and the
  * drained tail between per-map launches.  Work is ordered map by map (map 0
  * first), and within a map by row-block length (longest first) and then by
- * head.  Exception: with split phase 2 (n > 8192) and every map large enough
- * to fill the GPU alone (B * H_m * ceil(n/256) >= 1024), the maps run one
- * after another, each through its own three sweeps, which keeps a map's
- * projections in the last-level cache between its sweeps (5% faster phase 2
- * at n = 16K, three maps of 32 heads, on MI355X).  Results are the same
- * bits either way.
+ * head.  Exception: when the bf16 projections of all maps together exceed
+ * 256 MiB, the maps run one after another, each as larard_loss runs it
+ * (head groups, AUTO phase 2), which keeps a map's projections in the
+ * last-level cache between its sweeps (on MI355X: 5% faster phase 2 at
+ * n = 16K with three maps of 32 heads; 6.84 against 7.29 ms per step for
+ * the GQA 8K maps).  Results are the same bits either way.
  * ------------------------------------------------------------------------- */
 typedef struct {
   const void* x_t;   /* [B, H, n, d] teacher projections of this map (device) */

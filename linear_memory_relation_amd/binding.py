@@ -44,6 +44,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.larard_workspace_bytes.restype = ctypes.c_size_t
     lib.larard_loss_head_group.argtypes = [i32, i64, i64, i64, i64, i32]
     lib.larard_loss_head_group.restype = i64
+    lib.larard_loss_sweep_group.argtypes = [i32, i64, i64, i64, i64, i32]
+    lib.larard_loss_sweep_group.restype = i64
     lib.larard_workspace_layout.argtypes = [i32, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.larard_workspace_layout.restype = i32
     lib.larard_lse_fwd.argtypes = [vp, vp, i32, i64, i64, i64, i64, f32, i32, vp, vp, vp]
@@ -181,6 +183,14 @@ def workspace_bytes(B: int, H: int, n: int, dtype: int = BF16) -> int:
 def loss_head_group(B: int, H: int, n: int, d: int, dtype: int = BF16, cross: bool = False) -> int:
     """Heads per group of the whole-path calls (phase 1 and 2 per group of the B*H heads)."""
     g = int(load().larard_loss_head_group(dtype, B, H, n, d, 1 if cross else 0))
+    if g <= 0:
+        raise ValueError(f"invalid sizes B={B} H={H} n={n} d={d}")
+    return g
+
+
+def loss_sweep_group(B: int, H: int, n: int, d: int, dtype: int = BF16, cross: bool = False) -> int:
+    """Heads per phase-2 sub-group of the whole-path calls (within each head group)."""
+    g = int(load().larard_loss_sweep_group(dtype, B, H, n, d, 1 if cross else 0))
     if g <= 0:
         raise ValueError(f"invalid sizes B={B} H={H} n={n} d={d}")
     return g

@@ -144,13 +144,24 @@ larard_status run_kl_bwd(lmr::SweepArgs a, float loss_scale, int dx_mode, hipStr
 #define LMR_GROUP_MIB 256
 #endif
 constexpr int64_t kGroupBytes = int64_t(LMR_GROUP_MIB) << 20;
+// Phase 2 of a group runs in sub-groups of at most this many bytes of
+// projections (still at least kGroupGrid workgroups per sweep): the split
+// sweeps read them twice, the fused sweep twice within one launch.
+// Measured on MI355X, ms per step, phase 2 per group -> per sub-group of
+// 128 MiB: n = 16K split 25.70-25.79 -> 25.37-25.49, fused 26.23 -> 25.36-25.54;
+// n = 32K fused 102.5-103.1 -> 100.5; GQA 8K fused 6.92-6.94 -> 6.66-6.69;
+// 4K unchanged (one sub-group).
+#ifndef LMR_GROUP2_MIB
+#define LMR_GROUP2_MIB 128
+#endif
+constexpr int64_t kSweepGroupBytes = int64_t(LMR_GROUP2_MIB) << 20;
 constexpr int64_t kGroupGrid = 1024;
 
-int64_t group_of(bool fp32, bool cross, int64_t bh, int64_t n, int64_t d) {
+int64_t group_of(bool fp32, bool cross, int64_t bh, int64_t n, int64_t d, int64_t budget = kGroupBytes) {
   if (fp32) return bh;
   const int64_t per_head = (cross ? 4 : 2) * n * d * 2;
   const int64_t rows_blk = (n + 255) / 256;
-  int64_t g = per_head > 0 ? kGroupBytes / per_head : bh;
+  int64_t g = per_head > 0 ? budget / per_head : bh;
   if (rows_blk > 0) g = std::max(g, (kGroupGrid + rows_blk - 1) / rows_blk);
   return std::max<int64_t>(1, std::min(g, bh));
 }
@@ -174,15 +185,19 @@ lmr::SweepArgs head_slice(const lmr::SweepArgs& a, int64_t h0, int64_t cnt) {
   return g;
 }
 
-// Phase 1 and phase 2 of a whole-path call with a gradient, group by group.
+// Phase 1 and phase 2 of a whole-path call with a gradient, group by group;
+// within a group, phase 2 runs in sub-groups (larard_loss_sweep_group).
 larard_status run_grouped(const lmr::SweepArgs& a, float loss_scale, int dx_mode, hipStream_t st) {
   const int64_t g = head_group(a);
+  const int64_t g2 = group_of(a.fp32 != 0, a.cross != 0, a.bh, a.n, a.d, kSweepGroupBytes);
   for (int64_t h0 = 0; h0 < a.bh; h0 += g) {
     const lmr::SweepArgs part = head_slice(a, h0, std::min(g, a.bh - h0));
     const hipError_t e = lmr::launch_lse_fwd(part, st);
     if (e != hipSuccess) return hip_fail(e, "lse_fwd launch");
-    const larard_status s = run_kl_bwd(part, loss_scale, dx_mode, st);
-    if (s != LARARD_OK) return s;
+    for (int64_t k0 = 0; k0 < part.bh; k0 += g2) {
+      const larard_status s = run_kl_bwd(head_slice(part, k0, std::min(g2, part.bh - k0)), loss_scale, dx_mode, st);
+      if (s != LARARD_OK) return s;
+    }
   }
   return LARARD_OK;
 }
@@ -297,6 +312,12 @@ int64_t larard_loss_head_group(larard_dtype dtype, int64_t B, int64_t H, int64_t
   if (B < 1 || H < 1 || n < 0 || n > kMaxN || B > kMaxGrid / H || (d != 64 && d != 128)) return 0;
   if (dtype != LARARD_BF16 && dtype != LARARD_FP32) return 0;
   return group_of(dtype == LARARD_FP32, cross != 0, B * H, n, d);
+}
+
+int64_t larard_loss_sweep_group(larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d, int cross) {
+  if (B < 1 || H < 1 || n < 0 || n > kMaxN || B > kMaxGrid / H || (d != 64 && d != 128)) return 0;
+  if (dtype != LARARD_BF16 && dtype != LARARD_FP32) return 0;
+  return group_of(dtype == LARARD_FP32, cross != 0, B * H, n, d, kSweepGroupBytes);
 }
 
 larard_status larard_workspace_layout(larard_dtype dtype, int64_t B, int64_t H, int64_t n, size_t off[4]) {
@@ -538,22 +559,20 @@ larard_status larard_xy_loss(const void* x_t, const void* x_s, const void* y_t, 
 // ---------------------------------------------------------------------------
 // Several maps in one launch per phase (larard.h, larard_multi_loss).
 namespace {
-// Row blocks per head of the 8-wave sweeps, and the grid from which a map
-// fills the GPU on its own (four workgroups per CU).
-constexpr int64_t kSweepRows = 256;
-constexpr int64_t kMapGridAlone = 1024;
-// Split phase 2 with every map's own sweep grid at least kMapGridAlone
-// workgroups: the maps then run one after another, each through its three
-// sweeps.  At n = 16K (three maps of 32 heads) the single-launch row and
-// column sweeps over all maps took 5% longer than the maps' own launches in
-// sequence, whose second and third sweeps find the map's projections in the
-// last-level cache.
-bool maps_run_apart(const larard_map* maps, int n_maps, int64_t B, int64_t n, const lmr::SweepArgs& a0) {
-  if (use_fused(a0, LARARD_DX_AUTO)) return false;
-  const int64_t nblk = (n + kSweepRows - 1) / kSweepRows;
-  for (int m = 0; m < n_maps; ++m)
-    if (B * maps[m].H * nblk < kMapGridAlone) return false;
-  return true;
+// The maps run one after another, each as larard_loss runs it (head groups
+// and phase-2 sub-groups), when the projections of all maps together exceed
+// one head group's budget: a single launch per phase over all maps would
+// then re-read them from HBM in phase 2.  Measured on MI355X: at n = 16K
+// (three maps of 32 heads, 768 MiB) the single-launch row and column sweeps
+// took 5% longer than the maps' own launches in sequence; GQA 8K (Q over 64
+// heads, K and V over 16 each, 384 MiB) 7.29 ms per step in one launch per
+// phase against 6.84 for the maps apart.  Small sets (4K: 192 MiB) keep the
+// single launch, which saves the launch gaps and tails of short kernels
+// (1.77 against 1.87 ms).
+bool maps_run_apart(const larard_map* maps, int n_maps, int64_t B, int64_t n, int64_t d) {
+  int64_t bytes = 0;
+  for (int m = 0; m < n_maps; ++m) bytes += B * maps[m].H * n * d * 2 * 2;
+  return bytes > kGroupBytes;
 }
 }  // namespace
 // ---------------------------------------------------------------------------
@@ -648,13 +667,11 @@ larard_status larard_multi_loss(const larard_map* maps, int n_maps, larard_dtype
     if (e != hipSuccess) return hip_fail(e, "multi-map launch");
   } else if (with_dx == 0) {
     if ((e = lmr::launch_kl_fwd_multi(set, st)) != hipSuccess) return hip_fail(e, "multi-map kl_fwd launch");
-  } else if (maps_run_apart(maps, n_maps, B, n, set.map[0])) {
-    // Every map fills the GPU on its own: its three sweeps run back to back,
-    // while its projections are still in the last-level cache.
+  } else if (maps_run_apart(maps, n_maps, B, n, d)) {
     for (int m = 0; m < n_maps; ++m) {
       // grad_scale already carries the map's weight; run_kl_bwd sets it
       // from loss_scale, so pass the weighted scale.
-      if ((s = run_grouped(set.map[m], loss_scale * maps[m].weight, LARARD_DX_SPLIT, st)) != LARARD_OK) return s;
+      if ((s = run_grouped(set.map[m], loss_scale * maps[m].weight, LARARD_DX_AUTO, st)) != LARARD_OK) return s;
     }
   } else {
     if ((e = lmr::launch_lse_fwd_multi(set, st)) != hipSuccess) return hip_fail(e, "multi-map lse_fwd launch");

@@ -44,6 +44,8 @@ int main() {
   if (larard_loss_head_group(bf, big, big, 64, 128, 0) != 0) { std::printf("FAIL huge head group accepted\n"); ++g_fail; }
   if (larard_loss_head_group(bf, 1, 1, int64_t(1) << 24, 128, 1) != 1) { std::printf("FAIL head group max n\n"); ++g_fail; }
   if (larard_loss_head_group(bf, 1, 4, -1, 128, 0) != 0) { std::printf("FAIL negative n accepted\n"); ++g_fail; }
+  if (larard_loss_sweep_group(bf, 1, 32, 16384, 128, 0) != 16) { std::printf("FAIL sweep group 16K\n"); ++g_fail; }
+  if (larard_loss_sweep_group(bf, big, big, 64, 128, 0) != 0) { std::printf("FAIL huge sweep group accepted\n"); ++g_fail; }
   size_t off[4];
   expect("layout null", larard_workspace_layout(bf, 1, 1, 4, nullptr), LARARD_E_INVALID);
   expect("layout", larard_workspace_layout(bf, 2, 8, 8192, off), LARARD_OK);

@@ -300,4 +300,12 @@ def test_loss_head_group_sizes(lib):
     assert hg(0, 1, 16, 262144, 128, 0) == 2          # 128 MiB per head: 2 heads x 1024 row blocks
     assert hg(1, 1, 32, 32768, 128, 0) == 32          # fp32 precision kernels: one group
     assert hg(0, 1, 32, 0, 128, 0) == 32
+    sg = lib.larard_loss_sweep_group
+    sg.restype = ctypes.c_int64
+    sg.argtypes = hg.argtypes
+    assert sg(0, 1, 32, 16384, 128, 0) == 16          # 128 MiB of projections per phase-2 sub-group
+    assert sg(0, 1, 32, 32768, 128, 0) == 8           # 16 MiB per head; 128 row blocks x 8 = 1024
+    assert sg(0, 1, 32, 4096, 128, 0) == 32
+    assert sg(0, 2, 32, 8192, 128, 0) == 32           # 4 MiB per head
+    assert sg(1, 1, 32, 32768, 128, 0) == 32 and sg(0, 0, 32, 16384, 128, 0) == 0
     assert hg(0, 0, 32, 16384, 128, 0) == 0 and hg(0, 1, 32, 16384, 96, 0) == 0 and hg(7, 1, 32, 16, 64, 0) == 0

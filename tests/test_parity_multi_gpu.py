@@ -72,14 +72,14 @@ def test_multi_fp32(gpu_lib):
 
 
 def test_multi_large_maps_run_apart(gpu_lib):
-    """Split phase 2 (n > 8192) with every map filling the GPU alone (B*H*ceil(n/256)
-    >= 1024 workgroups): larard_multi_loss runs the maps one after another,
-    each through its own sweeps.  Loss and gradients must equal the per-map
-    calls bit for bit, and sampled gradient rows of one head per map match
-    the oracle."""
+    """Maps whose bf16 projections together exceed 256 MiB (here 2 x 64 heads at
+    n = 8448, d = 128: 554 MB): larard_multi_loss runs them one after another,
+    each as larard_loss would (head groups, split phase 2 above n = 8192).  Loss
+    and gradients must equal the per-map calls bit for bit, and sampled
+    gradient rows of one head per map match the oracle."""
     import torch
-    B, n, d, Hs, weights = 1, 8448, 64, (32, 32), (1.0, 0.5)
-    assert all(B * H * ((n + 255) // 256) >= 1024 for H in Hs)
+    B, n, d, Hs, weights = 1, 8448, 128, (64, 64), (1.0, 0.5)
+    assert sum(B * H * n * d * 4 for H in Hs) > 256 << 20
     host = _maps_gqa(B, n, d, Hs, seed=9)
     dev = [(to_device(a, "bf16"), to_device(b, "bf16")) for a, b in host]
     s = 1.0 / np.sqrt(d)
