@@ -155,14 +155,18 @@ constexpr int64_t kGroupBytes = int64_t(LMR_GROUP_MIB) << 20;
 #define LMR_GROUP2_MIB 128
 #endif
 constexpr int64_t kSweepGroupBytes = int64_t(LMR_GROUP2_MIB) << 20;
+#ifndef LMR_GROUP2_GRID
+#define LMR_GROUP2_GRID 1024
+#endif
 constexpr int64_t kGroupGrid = 1024;
 
-int64_t group_of(bool fp32, bool cross, int64_t bh, int64_t n, int64_t d, int64_t budget = kGroupBytes) {
+int64_t group_of(bool fp32, bool cross, int64_t bh, int64_t n, int64_t d, int64_t budget = kGroupBytes,
+                 int64_t grid = kGroupGrid) {
   if (fp32) return bh;
   const int64_t per_head = (cross ? 4 : 2) * n * d * 2;
   const int64_t rows_blk = (n + 255) / 256;
   int64_t g = per_head > 0 ? budget / per_head : bh;
-  if (rows_blk > 0) g = std::max(g, (kGroupGrid + rows_blk - 1) / rows_blk);
+  if (rows_blk > 0) g = std::max(g, (grid + rows_blk - 1) / rows_blk);
   return std::max<int64_t>(1, std::min(g, bh));
 }
 
@@ -189,7 +193,7 @@ lmr::SweepArgs head_slice(const lmr::SweepArgs& a, int64_t h0, int64_t cnt) {
 // within a group, phase 2 runs in sub-groups (larard_loss_sweep_group).
 larard_status run_grouped(const lmr::SweepArgs& a, float loss_scale, int dx_mode, hipStream_t st) {
   const int64_t g = head_group(a);
-  const int64_t g2 = group_of(a.fp32 != 0, a.cross != 0, a.bh, a.n, a.d, kSweepGroupBytes);
+  const int64_t g2 = group_of(a.fp32 != 0, a.cross != 0, a.bh, a.n, a.d, kSweepGroupBytes, LMR_GROUP2_GRID);
   for (int64_t h0 = 0; h0 < a.bh; h0 += g) {
     const lmr::SweepArgs part = head_slice(a, h0, std::min(g, a.bh - h0));
     const hipError_t e = lmr::launch_lse_fwd(part, st);
@@ -317,7 +321,7 @@ int64_t larard_loss_head_group(larard_dtype dtype, int64_t B, int64_t H, int64_t
 int64_t larard_loss_sweep_group(larard_dtype dtype, int64_t B, int64_t H, int64_t n, int64_t d, int cross) {
   if (B < 1 || H < 1 || n < 0 || n > kMaxN || B > kMaxGrid / H || (d != 64 && d != 128)) return 0;
   if (dtype != LARARD_BF16 && dtype != LARARD_FP32) return 0;
-  return group_of(dtype == LARARD_FP32, cross != 0, B * H, n, d, kSweepGroupBytes);
+  return group_of(dtype == LARARD_FP32, cross != 0, B * H, n, d, kSweepGroupBytes, LMR_GROUP2_GRID);
 }
 
 larard_status larard_workspace_layout(larard_dtype dtype, int64_t B, int64_t H, int64_t n, size_t off[4]) {
