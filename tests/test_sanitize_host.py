@@ -40,7 +40,7 @@ def test_abi_validation_is_clean_under_asan_and_ubsan(tmp_path):
     # the kernels, unchanged (linked, never launched)
     for src in ("kernels", "wide", "proj"):
         _run([HIPCC, *common, "-c", os.path.join(CSRC, src + ".hip"), "-o", src + ".o"], tmp_path)
-    # the driver and the link, host only
+    # the check program and the link, host only
     san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
     _run([CLANG, "-std=c++17", "-g", "-I", INCLUDE, *san, "-c", os.path.join(ROOT, "tests", "sanitize",
                                                                              "abi_check.cpp"), "-o", "drv.o"],
