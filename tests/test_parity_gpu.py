@@ -397,14 +397,16 @@ def test_auto_mode_choice(gpu_lib, n, expect):
 
 
 @pytest.mark.parametrize("mode", MODES)
-def test_head_groups_match_one_launch(gpu_lib, mode):
-    """larard_loss runs phase 1 and phase 2 head group by head group (here 64
-    heads at n = 8448, d = 128: groups of 62 and 2, larard_loss_head_group);
-    its loss and gradient equal those of the phase entry points launched once
-    over all heads, bit for bit."""
+@pytest.mark.parametrize("B,H", [(1, 64), (3, 24)])
+def test_head_groups_match_one_launch(gpu_lib, mode, B, H):
+    """larard_loss runs phase 1 per head group and phase 2 per sub-group
+    (n = 8448, d = 128: groups of 62 heads of the flattened B*H, sub-groups of
+    32; with B = 3, H = 24 the boundaries fall inside batches); its loss and
+    gradient equal those of the phase entry points launched once over all
+    heads, bit for bit."""
     import torch
-    B, H, n, d = 1, 64, 8448, 128
-    assert gpu_lib.loss_head_group(B, H, n, d) == 62
+    n, d = 8448, 128
+    assert gpu_lib.loss_head_group(B, H, n, d) == 62 and gpu_lib.loss_sweep_group(B, H, n, d) == 32
     xt, xs = random_pair(B, H, n, d, 0.3, seed=21)
     a, b = to_device(xt, "bf16"), to_device(xs, "bf16")
     s = 1.0 / np.sqrt(d)
